@@ -1,0 +1,193 @@
+"""CPU oracle for Stream-Factorized Attention (Hidden Decoding).
+
+TEST INFRASTRUCTURE ONLY.  This package is the checker that the GPU library is
+held against; it is not part of the product.  Only ``tests/``, the smoke check
+in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` import it.  It
+shares no code with ``latent_sequence_length_amd`` and never imports it.
+
+Two independent implementations live here:
+
+* ``hd_oracle.c`` (wrapped below through ctypes): the plain definition of every
+  step, evaluated in double precision with keys visited in ascending order.
+* ``brute.py``: a NumPy float64 brute force that materialises the nL x nL mask
+  straight from the 1-based index maps of the pages, for tiny shapes.
+
+Sources (WeLM blog "Hidden Decoding at Scale", section "Method Recap and New
+Designs"): the expansion equation S_t = E_k(x_i) with t = (i-1)n + k; the index
+maps i(t) = ceil(t/n), s(t) = (t-1) mod n + 1 and Figure 2's three masks; the
+per-stream KV cache retained for decoding.
+
+Every function here is pinned by ``tests/test_oracle_*.py`` against library
+routines, closed forms, invariants and hand-worked golden values.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhd_oracle.so")
+
+INTRA, CROSS = 0, 1
+_F32, _BF16 = 0, 1
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH) or (
+        os.path.getmtime(LIB_PATH) < os.path.getmtime(os.path.join(HERE, "hd_oracle.c"))
+    ):
+        from . import build as _build  # compiling the checker is not using it
+
+        _build.build()
+    lib = _configure(ctypes.CDLL(LIB_PATH))
+    _lib = lib
+    return lib
+
+
+def _configure(lib):
+    """Declare the C signatures on a loaded oracle library."""
+    P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.oracle_expand_embed.argtypes = [P, I, I, I, P, I64, I64, P]
+    lib.oracle_visible.argtypes = [I64, I64, I, I, I64]
+    lib.oracle_sfa_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, I64, P, P]
+    lib.oracle_sfa_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
+    lib.oracle_sfa_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, I64, D, P]
+    lib.oracle_decode_append.argtypes = [P, P, P, I, I, I, I, I, I64]
+    for f in (lib.oracle_expand_embed, lib.oracle_visible, lib.oracle_sfa_rows,
+              lib.oracle_sfa_fwd, lib.oracle_sfa_decode, lib.oracle_decode_append):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _buf(x):
+    """Return (contiguous numpy array, dtype code) for float32 / bfloat16 data.
+
+    Accepts numpy float32 arrays, numpy uint16 arrays holding raw bfloat16
+    bits, or CPU torch tensors of dtype float32 / bfloat16."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu().contiguous()
+            if x.dtype == torch.bfloat16:
+                return np.ascontiguousarray(x.view(torch.int16).numpy().view(np.uint16)), _BF16
+            if x.dtype == torch.float32:
+                return np.ascontiguousarray(x.numpy()), _F32
+            raise TypeError(f"oracle input dtype {x.dtype} not float32/bfloat16")
+    except ImportError:  # pragma: no cover
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        return x, _F32
+    if x.dtype == np.uint16:
+        return x, _BF16
+    raise TypeError(f"oracle input dtype {x.dtype} not float32 / uint16(bf16 bits)")
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def visible(tq, tk, n, mode, window=0):
+    """Figure 2 predicate on 0-based expanded positions (1 = visible)."""
+    return _load().oracle_visible(int(tq), int(tk), int(n), int(mode), int(window))
+
+
+def expand_embed(ids, tables):
+    """out[b, i*n+s, :] = tables[s][ids[b,i], :] as a raw byte copy.
+
+    ids: int32 [B, L]; tables: list of n arrays [V, D] of one dtype.
+    Returns a numpy array [B, n*L, D] of the tables' dtype (bf16 as uint16 bits)."""
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    bufs = [_buf(t)[0] for t in tables]
+    B, L = ids.shape
+    n = len(bufs)
+    V, D = bufs[0].shape
+    for t in bufs:
+        if t.shape != (V, D) or t.dtype != bufs[0].dtype:
+            raise ValueError("tables must share shape and dtype")
+    out = np.empty((B, n * L, D), dtype=bufs[0].dtype)
+    ptrs = (ctypes.c_void_p * n)(*[t.ctypes.data for t in bufs])
+    rc = _load().oracle_expand_embed(_p(ids), B, L, n, ptrs, V, D * bufs[0].itemsize, _p(out))
+    if rc:
+        raise ValueError("id outside [0, V)")
+    return out
+
+
+def sfa_rows(q, k, v, n, mode, window=0, scale=0.0, rows=None):
+    """Attention output (float64) for selected flat query rows r = (b*nL+t)*Hq+h.
+
+    q [B, nL, Hq, d], k/v [B, nL, Hkv, d].  Returns (o [nrows, d], lse [nrows])."""
+    qb, dt = _buf(q)
+    kb, dt2 = _buf(k)
+    vb, dt3 = _buf(v)
+    if not (dt == dt2 == dt3):
+        raise TypeError("q, k, v must share a dtype")
+    B, nL, Hq, d = qb.shape
+    Hkv = kb.shape[2]
+    if nL % n:
+        raise ValueError("sequence length not a multiple of n")
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    rc = _load().oracle_sfa_rows(_p(qb), _p(kb), _p(vb), dt, B, nL // n, n, Hq, Hkv, d,
+                                 int(mode), int(window), float(scale), _p(rows), rows.size,
+                                 _p(o), _p(lse))
+    if rc:
+        raise ValueError("oracle_sfa_rows rejected its arguments")
+    return o, lse
+
+
+def sfa_fwd(q, k, v, n, mode, window=0, scale=0.0):
+    """Full prefill: returns (o [B, nL, Hq, d] float64, lse [B, Hq, nL] float64)."""
+    qb, dt = _buf(q)
+    kb, _ = _buf(k)
+    vb, _ = _buf(v)
+    B, nL, Hq, d = qb.shape
+    Hkv = kb.shape[2]
+    if nL % n:
+        raise ValueError("sequence length not a multiple of n")
+    o = np.empty((B, nL, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, nL), dtype=np.float64)
+    rc = _load().oracle_sfa_fwd(_p(qb), _p(kb), _p(vb), dt, B, nL // n, n, Hq, Hkv, d,
+                                int(mode), int(window), float(scale), _p(o), _p(lse))
+    if rc:
+        raise ValueError("oracle_sfa_fwd rejected its arguments")
+    return o, lse
+
+
+def sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, scale=0.0):
+    """One decode step; returns o [B, n, Hq, d] float64 (caches are not modified)."""
+    qb, dt = _buf(q)
+    knb, _ = _buf(k_new)
+    vnb, _ = _buf(v_new)
+    kcb, _ = _buf(k_cache)
+    vcb, _ = _buf(v_cache)
+    lens = np.ascontiguousarray(np.asarray(cache_len, dtype=np.int32))
+    B, n, Hq, d = qb.shape
+    T_cap, Hkv = kcb.shape[1], kcb.shape[3]
+    o = np.empty((B, n, Hq, d), dtype=np.float64)
+    rc = _load().oracle_sfa_decode(_p(qb), _p(knb), _p(vnb), _p(kcb), _p(vcb), dt, _p(lens),
+                                   T_cap, B, n, Hq, Hkv, d, int(mode), int(window),
+                                   float(scale), _p(o))
+    if rc:
+        raise ValueError("oracle_sfa_decode rejected its arguments")
+    return o
+
+
+def decode_append(x_new, cache, cache_len):
+    """Return a copy of cache with x_new written at token cache_len[b] (bytewise)."""
+    xb, _ = _buf(x_new)
+    cb, _ = _buf(cache)
+    out = cb.copy()
+    lens = np.ascontiguousarray(np.asarray(cache_len, dtype=np.int32))
+    B, T_cap, n, Hkv, d = out.shape
+    rc = _load().oracle_decode_append(_p(xb), _p(out), _p(lens), T_cap, B, n, Hkv, d, out.itemsize)
+    if rc:
+        raise ValueError("cache_len outside [0, T_cap)")
+    return out

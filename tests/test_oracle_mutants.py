@@ -1,0 +1,66 @@
+"""The pins are strong enough: plausible mistakes planted in a copy of the C
+oracle (on the CPU, in a temporary build) must each fail at least one pin.
+
+Nothing here touches the real oracle library or the GPU path; each mutant is a
+text edit of ``oracle/hd_oracle.c`` compiled into a temporary directory.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "hd_oracle.c")
+INTRA, CROSS = 0, 1
+
+MUTANTS = [
+    ("intra sees one future token", "if (ik > iq) return 0;", "if (ik > iq + 1) return 0;",
+     [pins.test_golden_masks_figure2, pins.test_mask_exhaustive_c_vs_onebased]),
+    ("intra drops the diagonal", "if (ik > iq) return 0;", "if (ik >= iq && iq > 0) return 0;",
+     [pins.test_golden_masks_figure2]),
+    ("streams not separated", "if (sk != sq) return 0;", "",
+     [pins.test_intra_is_n_independent_causal]),
+    ("intra window off by one", "if (W > 0 && iq - ik >= W) return 0;",
+     "if (W > 0 && iq - ik > W) return 0;", [pins.test_golden_masks_figure2]),
+    ("cross window in tokens, not positions", "tq - tk >= (int64_t)n * W", "tq - tk >= W",
+     [pins.test_golden_masks_figure2, lambda o: pins.test_windows_are_banded_sdpa(o, 2)]),
+    ("GQA head map modulo", "int64_t hk = h / g;", "int64_t hk = h % Hkv;",
+     [pins.test_gqa_equals_repeated_mha]),
+    ("scale dropped", "scores[j] = scale * dot;", "scores[j] = dot;",
+     [lambda o: pins.test_n1_is_textbook_causal(o, CROSS)]),
+    ("key head offset dropped", "koff[tk] = ((b * nL + tk) * Hkv + hk) * d;",
+     "koff[tk] = ((b * nL + tk) * Hkv) * d;",
+     [lambda o: pins.test_n1_is_textbook_causal(o, INTRA), pins.test_c_oracle_matches_brute_force]),
+    ("value read from key", "o[c] += p * load_elem(v, dtype, krow_off[j] + c);",
+     "o[c] += p * load_elem(k, dtype, krow_off[j] + c);",
+     [pins.test_worked_example_closed_form]),
+    ("lse without max shift", "*lse = m + log(l);", "*lse = log(l);",
+     [pins.test_lse_matches_logsumexp_and_scale]),
+    ("decode reads stale cache row for the new token", "if (tok < len) {", "if (tok <= len && tok < T_cap) {",
+     [lambda o: pins.test_decode_equals_prefill_rows(o, CROSS, 0)]),
+    ("expansion stream-major", "(((int64_t)b * L + i) * n + s) * row_bytes",
+     "(((int64_t)b * n + s) * L + i) * row_bytes", [pins.test_expand_golden_order]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,checks", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, checks):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for '{name}' must occur once"
+    mut = tmp_path / "mut.c"
+    mut.write_text(src.replace(old, new))
+    lib_path = str(tmp_path / "libmut.so")
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fopenmp", "-fPIC", "-shared", str(mut), "-o", lib_path, "-lm"],
+                   check=True)
+    lib = oracle._configure(ctypes.CDLL(lib_path))
+    saved = oracle._load()
+    oracle._lib = lib
+    try:
+        for check in checks:
+            with pytest.raises((AssertionError, ValueError)):
+                check(oracle)
+    finally:
+        oracle._lib = saved

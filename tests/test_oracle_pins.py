@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test ties the oracle to something independent: the hand-written Figure 2
+masks, a library routine (torch's scaled_dot_product_attention and embedding,
+NumPy fancy indexing), a closed form, or an invariant the definitions imply.
+All run on the CPU.  Source of the definitions: WeLM blog "Hidden Decoding at
+Scale", section "Method Recap and New Designs" (expansion equation, index maps,
+Figure 2, per-stream KV retention).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from latent_sequence_length_amd import synth
+from oracle import brute
+from tests.golden_io import mask_from_rows, read_blocks
+
+INTRA, CROSS = 0, 1
+
+
+def _rand(shape, seed, dtype=torch.float32):
+    return synth.normal(shape, seed, dtype)
+
+
+def sdpa64(q, k, v, attn_mask=None, causal=False, scale=None):
+    """torch SDPA in float64 on [B, T, H, d] tensors with GQA by repetition."""
+    q64, k64, v64 = (x.double().permute(0, 2, 1, 3) for x in (q, k, v))
+    g = q64.shape[1] // k64.shape[1]
+    k64 = k64.repeat_interleave(g, dim=1)
+    v64 = v64.repeat_interleave(g, dim=1)
+    out = F.scaled_dot_product_attention(q64, k64, v64, attn_mask=attn_mask, is_causal=causal, scale=scale)
+    return out.permute(0, 2, 1, 3).contiguous()
+
+
+# --------------------------------------------------------------------------
+# Mask predicate and index maps
+# --------------------------------------------------------------------------
+
+def test_golden_masks_figure2(oracle):
+    blocks = read_blocks("fig2_masks_n2_L3.txt")
+    n, L = 2, 3
+    for header, rows in blocks.items():
+        if not header.startswith("mask"):
+            continue
+        _, mode_s, w_s = header.split()
+        mode = INTRA if mode_s == "intra" else CROSS
+        W = int(w_s.split("=")[1])
+        want = mask_from_rows(rows)
+        got_c = np.array([[oracle.visible(tq, tk, n, mode, W) for tk in range(n * L)]
+                          for tq in range(n * L)], dtype=bool)
+        np.testing.assert_array_equal(got_c, want, err_msg=header)
+        np.testing.assert_array_equal(brute.mask(n, L, mode, W), want, err_msg=header)
+
+
+def test_golden_index_maps():
+    blocks = read_blocks("fig2_masks_n2_L3.txt")
+    for line in blocks["index n=4"]:
+        t, i, s = map(int, line.split())
+        assert brute.token_index(t, 4) == i and brute.stream_index(t, 4) == s
+
+
+def test_mask_exhaustive_c_vs_onebased(oracle):
+    """0-based C predicate == explicit mask built from the 1-based index maps."""
+    for n, L, W, mode in itertools.product(range(1, 5), range(1, 9), range(0, 4), (INTRA, CROSS)):
+        want = brute.mask(n, L, mode, W)
+        got = np.array([[oracle.visible(tq, tk, n, mode, W) for tk in range(n * L)]
+                        for tq in range(n * L)], dtype=bool)
+        assert np.array_equal(got, want), (n, L, W, mode)
+
+
+def test_mask_structure_invariants():
+    """intra = cross restricted to the same stream (any window); n=1: intra == cross."""
+    for n, L, W in itertools.product(range(1, 5), range(1, 7), range(0, 4)):
+        intra, cross = brute.mask(n, L, INTRA, W), brute.mask(n, L, CROSS, W)
+        t = np.arange(n * L)
+        same = (t[:, None] % n) == (t[None, :] % n)
+        if W == 0:
+            assert np.array_equal(intra, cross & same)
+        assert not (intra & ~same).any()
+        assert np.tril(np.ones_like(cross)).astype(bool)[cross].all()
+        assert np.diag(intra).all() and np.diag(cross).all()
+        if n == 1:
+            assert np.array_equal(intra, cross)
+
+
+# --------------------------------------------------------------------------
+# Expansion
+# --------------------------------------------------------------------------
+
+def test_expand_golden_order(oracle):
+    blocks = read_blocks("fig2_masks_n2_L3.txt")
+    tabs = [np.arange(10 * 3, dtype=np.float32).reshape(10, 3) + 1000 * (s + 1) for s in range(2)]
+    ids = np.array([[7, 2]], dtype=np.int32)
+    out = oracle.expand_embed(ids, tabs)
+    for line in blocks["expand n=2 L=2"]:
+        t, table, token = map(int, line.split())
+        np.testing.assert_array_equal(out[0, t - 1], tabs[table - 1][ids[0, token - 1]])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_expand_deinterleave_identity(oracle, dtype):
+    n, V, D, B, L = 3, 50, 24, 2, 9
+    tabs = synth.tables(n, V, D, dtype)
+    ids = synth.token_ids(B, L, V, force_edges=True)
+    out = oracle.expand_embed(ids.numpy(), tabs)
+    for s in range(n):
+        want = tabs[s][ids.long()]  # library gather
+        want = want.view(torch.int16).numpy().view(np.uint16) if dtype == torch.bfloat16 else want.numpy()
+        np.testing.assert_array_equal(out[:, s::n], want)
+
+
+def test_expand_n1_is_embedding(oracle):
+    V, D = 40, 16
+    tab = synth.tables(1, V, D, torch.float32)
+    ids = synth.token_ids(3, 11, V)
+    out = oracle.expand_embed(ids.numpy(), tab)
+    np.testing.assert_array_equal(out, F.embedding(ids.long(), tab[0]).numpy())
+
+
+def test_expand_rejects_bad_ids(oracle):
+    tab = synth.tables(2, 10, 4, torch.float32)
+    with pytest.raises(ValueError):
+        oracle.expand_embed(np.array([[0, 10]], dtype=np.int32), tab)
+    with pytest.raises(ValueError):
+        oracle.expand_embed(np.array([[-1]], dtype=np.int32), tab)
+
+
+# --------------------------------------------------------------------------
+# Attention: library special cases
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [INTRA, CROSS])
+def test_n1_is_textbook_causal(oracle, mode):
+    B, L, Hq, Hkv, d = 2, 37, 4, 2, 16
+    q, k, v = (_rand((B, L, h, d), s) for s, h in ((0, Hq), (1, Hkv), (2, Hkv)))
+    o, _ = oracle.sfa_fwd(q, k, v, 1, mode)
+    np.testing.assert_allclose(o, sdpa64(q, k, v, causal=True).numpy(), rtol=0, atol=1e-12)
+
+
+def test_intra_is_n_independent_causal(oracle):
+    B, L, n, Hq, Hkv, d = 1, 23, 4, 4, 2, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    o, _ = oracle.sfa_fwd(q, k, v, n, INTRA)
+    for s in range(n):
+        want = sdpa64(q[:, s::n], k[:, s::n], v[:, s::n], causal=True).numpy()
+        np.testing.assert_allclose(o[:, s::n], want, rtol=0, atol=1e-12)
+
+
+def test_cross_is_dense_causal(oracle):
+    B, L, n, Hq, Hkv, d = 2, 13, 3, 2, 1, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    o, _ = oracle.sfa_fwd(q, k, v, n, CROSS)
+    np.testing.assert_allclose(o, sdpa64(q, k, v, causal=True).numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [1, 2, 5])
+def test_windows_are_banded_sdpa(oracle, W):
+    B, L, n, Hq, Hkv, d = 1, 17, 3, 2, 2, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    # intra: per-stream band of W tokens
+    o, _ = oracle.sfa_fwd(q, k, v, n, INTRA, W)
+    i = torch.arange(L)
+    band = (i[:, None] >= i[None, :]) & (i[:, None] - i[None, :] < W)
+    for s in range(n):
+        want = sdpa64(q[:, s::n], k[:, s::n], v[:, s::n], attn_mask=band).numpy()
+        np.testing.assert_allclose(o[:, s::n], want, rtol=0, atol=1e-12)
+    # cross: band of n*W expanded positions
+    o, _ = oracle.sfa_fwd(q, k, v, n, CROSS, W)
+    t = torch.arange(n * L)
+    band = (t[:, None] >= t[None, :]) & (t[:, None] - t[None, :] < n * W)
+    np.testing.assert_allclose(o, sdpa64(q, k, v, attn_mask=band).numpy(), rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_repeated_mha(oracle):
+    B, L, n, Hq, Hkv, d = 1, 11, 2, 6, 2, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    g = Hq // Hkv
+    for mode in (INTRA, CROSS):
+        o, _ = oracle.sfa_fwd(q, k, v, n, mode)
+        o2, _ = oracle.sfa_fwd(q, k.repeat_interleave(g, 2), v.repeat_interleave(g, 2), n, mode)
+        np.testing.assert_array_equal(o, o2)
+
+
+def test_lse_matches_logsumexp_and_scale(oracle):
+    B, L, n, H, d = 1, 9, 2, 2, 8
+    q, k, v = synth.qkv(B, L, n, H, H, d, torch.float32)
+    for mode, W, scale in ((INTRA, 0, 0.0), (CROSS, 2, 0.3)):
+        _, lse = oracle.sfa_fwd(q, k, v, n, mode, W, scale)
+        m = torch.from_numpy(brute.mask(n, L, mode, W))
+        sc = (scale if scale > 0 else 1 / math.sqrt(d))
+        s = torch.einsum("bthd,bshd->bhts", q.double(), k.double()) * sc
+        s = s.masked_fill(~m, float("-inf"))
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Attention: closed forms and invariants
+# --------------------------------------------------------------------------
+
+def test_window1_intra_returns_v(oracle):
+    q, k, v = synth.qkv(1, 10, 3, 4, 2, 8, torch.float32)
+    o, _ = oracle.sfa_fwd(q, k, v, 3, INTRA, 1)
+    np.testing.assert_array_equal(o, v.double().repeat_interleave(2, 2).numpy())
+
+
+def test_zero_query_prefix_means(oracle):
+    B, L, n, Hq, Hkv, d = 1, 12, 3, 2, 1, 4
+    _, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    q = torch.zeros(B, n * L, Hq, d)
+    v64 = v.double()
+    # intra: mean of stream s's values over tokens 0..i
+    o, lse = oracle.sfa_fwd(q, k, v, n, INTRA)
+    for s in range(n):
+        vs = v64[:, s::n, 0]
+        mean = vs.cumsum(1) / torch.arange(1, L + 1, dtype=torch.float64)[None, :, None]
+        for h in range(Hq):
+            np.testing.assert_allclose(o[:, s::n, h], mean.numpy(), rtol=0, atol=1e-13)
+    # lse with zero scores = log(number of visible keys)
+    np.testing.assert_allclose(lse[0, 0, :], np.log(np.arange(n * L) // n + 1), atol=1e-13)
+    # cross: positional prefix mean
+    o, lse = oracle.sfa_fwd(q, k, v, n, CROSS)
+    mean = v64[:, :, 0].cumsum(1) / torch.arange(1, n * L + 1, dtype=torch.float64)[None, :, None]
+    np.testing.assert_allclose(o[:, :, 0], mean.numpy(), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0, :], np.log(np.arange(n * L) + 1), atol=1e-13)
+
+
+def test_worked_example_closed_form(oracle):
+    """n=2, L=2, d=1, scale 1: every output written out by hand as a softmax."""
+    qv = [0.5, -1.0, 2.0, 0.25]
+    kv = [1.0, 2.0, -0.5, 3.0]
+    vv = [10.0, 20.0, 30.0, 40.0]
+    q = torch.tensor(qv).view(1, 4, 1, 1)
+    k = torch.tensor(kv).view(1, 4, 1, 1)
+    v = torch.tensor(vv).view(1, 4, 1, 1)
+    e = math.exp
+
+    def sm(t, keys):
+        w = [e(qv[t] * kv[j]) for j in keys]
+        return sum(wi * vv[j] for wi, j in zip(w, keys)) / sum(w)
+
+    o, _ = oracle.sfa_fwd(q, k, v, 2, INTRA, 0, 1.0)
+    want = [sm(0, [0]), sm(1, [1]), sm(2, [0, 2]), sm(3, [1, 3])]
+    np.testing.assert_allclose(o[0, :, 0, 0], want, rtol=1e-15)
+    o, _ = oracle.sfa_fwd(q, k, v, 2, CROSS, 0, 1.0)
+    want = [sm(0, [0]), sm(1, [0, 1]), sm(2, [0, 1, 2]), sm(3, [0, 1, 2, 3])]
+    np.testing.assert_allclose(o[0, :, 0, 0], want, rtol=1e-15)
+    o, _ = oracle.sfa_fwd(q, k, v, 2, CROSS, 1, 1.0)
+    want = [sm(0, [0]), sm(1, [0, 1]), sm(2, [1, 2]), sm(3, [2, 3])]
+    np.testing.assert_allclose(o[0, :, 0, 0], want, rtol=1e-15)
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (INTRA, 3), (CROSS, 2)])
+def test_constant_v_and_convex_hull(oracle, mode, W):
+    B, L, n, Hq, Hkv, d = 1, 15, 3, 4, 2, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    c = torch.full_like(v, 0.375)
+    o, _ = oracle.sfa_fwd(q, k, c, n, mode, W)
+    np.testing.assert_allclose(o, 0.375, rtol=0, atol=1e-15)
+    o, _ = oracle.sfa_fwd(q, k, v, n, mode, W)
+    m = brute.mask(n, L, mode, W)
+    vv = v.double().numpy()
+    for t in range(n * L):
+        vis = vv[0, m[t]]  # [nvis, Hkv, d]
+        for h in range(Hq):
+            lo, hi = vis[:, h // 2].min(0), vis[:, h // 2].max(0)
+            assert (o[0, t, h] >= lo - 1e-12).all() and (o[0, t, h] <= hi + 1e-12).all()
+
+
+def test_stream_permutation_equivariance(oracle):
+    B, L, n, Hq, Hkv, d = 1, 9, 4, 2, 2, 8
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+    perm = [2, 0, 3, 1]
+    idx = torch.tensor([i * n + perm[s] for i in range(L) for s in range(n)])
+    o, _ = oracle.sfa_fwd(q, k, v, n, INTRA)
+    op, _ = oracle.sfa_fwd(q[:, idx], k[:, idx], v[:, idx], n, INTRA)
+    np.testing.assert_array_equal(op, o[:, idx.numpy()])
+
+
+def test_c_oracle_matches_brute_force(oracle):
+    for (B, L, n, Hq, Hkv, d), mode, W in itertools.product(
+            [(1, 64, 2, 4, 4, 32), (2, 7, 3, 4, 2, 8), (1, 5, 1, 2, 1, 16)],
+            (INTRA, CROSS), (0, 1, 3)):
+        q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.float32)
+        o, lse = oracle.sfa_fwd(q, k, v, n, mode, W)
+        ob, lseb = brute.attention(q.numpy(), k.numpy(), v.numpy(), n, mode, W)
+        np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, lseb, rtol=0, atol=1e-12)
+
+
+def test_bf16_inputs_widen_exactly(oracle):
+    q, k, v = synth.qkv(1, 8, 2, 2, 1, 16, torch.bfloat16)
+    o16, _ = oracle.sfa_fwd(q, k, v, 2, CROSS)
+    o32, _ = oracle.sfa_fwd(q.float(), k.float(), v.float(), 2, CROSS)
+    np.testing.assert_array_equal(o16, o32)
+
+
+def test_rows_subset_matches_full(oracle):
+    q, k, v = synth.qkv(2, 10, 2, 4, 2, 8, torch.float32)
+    o, lse = oracle.sfa_fwd(q, k, v, 2, INTRA, 3)
+    rows = np.array([0, 5, 17, 79, 80, 159], dtype=np.int64)
+    orow, lrow = oracle.sfa_rows(q, k, v, 2, INTRA, 3, rows=rows)
+    np.testing.assert_array_equal(orow, o.reshape(-1, 8)[rows])
+    b, t, h = rows // (20 * 4), (rows // 4) % 20, rows % 4
+    np.testing.assert_array_equal(lrow, lse[b, h, t])
+
+
+# --------------------------------------------------------------------------
+# Decode over the retained per-stream cache
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (INTRA, 2), (CROSS, 1)])
+def test_decode_equals_prefill_rows(oracle, mode, W):
+    B, n, Hq, Hkv, d, T_cap = 3, 3, 4, 2, 8, 9
+    q, kn, vn, kc, vc = synth.decode_inputs(B, n, Hq, Hkv, d, T_cap, torch.float32)
+    lens = [0, 4, 8]
+    o = oracle.sfa_decode(q, kn, vn, kc, vc, lens, mode, W)
+    for b, ln in enumerate(lens):
+        L = ln + 1
+        kseq = torch.cat([kc[b, :ln], kn[b:b + 1]], 0).reshape(1, L * n, Hkv, d)
+        vseq = torch.cat([vc[b, :ln], vn[b:b + 1]], 0).reshape(1, L * n, Hkv, d)
+        qseq = torch.zeros(1, L * n, Hq, d)
+        qseq[0, ln * n:] = q[b]
+        of, _ = oracle.sfa_fwd(qseq, kseq, vseq, n, mode, W)
+        np.testing.assert_allclose(o[b], of[0, ln * n:], rtol=0, atol=1e-14)
+
+
+def test_decode_ignores_cache_rows_beyond_len(oracle):
+    B, n, Hq, Hkv, d, T_cap = 2, 2, 2, 1, 8, 6
+    q, kn, vn, kc, vc = synth.decode_inputs(B, n, Hq, Hkv, d, T_cap, torch.float32)
+    lens = [2, 3]
+    o1 = oracle.sfa_decode(q, kn, vn, kc, vc, lens, CROSS)
+    kc2, vc2 = kc.clone(), vc.clone()
+    kc2[0, 2:] = 1e30
+    vc2[1, 3:] = float("nan")
+    o2 = oracle.sfa_decode(q, kn, vn, kc2, vc2, lens, CROSS)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_decode_append_bytes(oracle):
+    B, n, Hkv, d, T_cap = 3, 2, 2, 4, 5
+    _, kn, _, kc, _ = synth.decode_inputs(B, n, 2, Hkv, d, T_cap, torch.bfloat16)
+    lens = [0, 2, 4]
+    out = oracle.decode_append(kn, kc, lens)
+    want = kc.clone()
+    for b, ln in enumerate(lens):
+        want[b, ln] = kn[b]
+    np.testing.assert_array_equal(out, want.view(torch.int16).numpy().view(np.uint16))
+    with pytest.raises(ValueError):
+        oracle.decode_append(kn, kc, [0, 5, 1])
