@@ -1,0 +1,255 @@
+"""Benchmark of the Stream-Factorized Attention hot path on one MI355X.
+
+One step = one pass over every step of the hot path on synthetic inputs that
+are already resident in HBM:
+  expand-embed   64 sequences x 1 token x 4 streams from 4 tables 160000 x 7168 bf16
+  intra prefill  n=4, L=4096 (nL=16384), 32 q / 8 kv heads, d=128, bf16   <- headline
+  intra prefill  n=1, L=4096 control (for the n=4 / n=1 time ratio)
+  cross prefill  same shapes as the headline, dense causal over 16384 positions
+  decode         64 sequences, 8192 cached tokens x 4 streams, 32 q / 8 kv heads,
+                 intra and cross (one new token, 4 stream queries each)
+Each call is timed with HIP events on the stream it is launched on.  The
+headline value is useful TFLOP/s of the intra-stream prefill (4*d*Hq FLOPs per
+visible query/key pair).  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from latent_sequence_length_amd import hd, synth
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
+    ap.add_argument("--long", action="store_true", help="also time the 32k-token (nL=131072) layers")
+    ap.add_argument("--only", default="", help="comma list of components to run (profiling)")
+    return ap.parse_args()
+
+
+class Timer:
+    """Accumulates HIP-event durations of launches on the current stream."""
+
+    def __init__(self):
+        self.ms = {}
+        self.pending = []
+
+    def run(self, name, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pending.append((name, s, e))
+
+    def collect(self):
+        torch.cuda.synchronize()
+        for name, s, e in self.pending:
+            self.ms.setdefault(name, []).append(s.elapsed_time(e))
+        self.pending = []
+
+
+def cpu_baseline(budget_s):
+    """Time the oracle on a bounded random sample of the headline workload."""
+    import oracle
+
+    c = synth.INTRA_4K
+    q, k, v = synth.qkv(c.B, c.L, c.n, c.Hq, c.Hkv, c.d, c.dtype, "cpu")
+    nL = c.n * c.L
+    rng = np.random.default_rng(123)
+    oracle.sfa_rows(q, k, v, c.n, c.mode, c.window, rows=np.array([0], dtype=np.int64))  # load + warm
+    flops = 0.0
+    rows_done = 0
+    t0 = time.perf_counter()
+    batch = 256
+    while time.perf_counter() - t0 < budget_s:
+        rows = rng.integers(0, c.B * nL * c.Hq, batch).astype(np.int64)
+        oracle.sfa_rows(q, k, v, c.n, c.mode, c.window, rows=rows)
+        t = (rows // c.Hq) % nL
+        visible = t // c.n + 1  # intra, no window: tokens 0..i of the query's stream
+        flops += float(4 * c.d * visible.sum())
+        rows_done += batch
+        batch = min(batch * 2, 8192)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{rows_done} random query rows of the n=4 L=4096 intra-stream prefill "
+                  f"({rows_done / (c.B * nL * c.Hq):.2%} of all rows), {dt:.1f} s, double-precision C oracle",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    only = set(x for x in args.only.split(",") if x)
+    want = (lambda name: not only or name in only)
+
+    I = synth.INTRA_4K
+    I1 = synth.INTRA_4K_N1
+    X = synth.CROSS_4K
+    Dc = synth.DECODE_8K
+    E = synth.EMBED_DECODE
+
+    comps = {}   # name -> (callable, useful flops, algorithmic bytes)
+
+    if want("intra_n4"):
+        q, k, v = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+        o = torch.empty_like(q)
+        fl = synth.useful_flops(I.B, I.L, I.n, I.Hq, I.d, 0)
+        by = 2 * (2 * q.numel() + k.numel() + v.numel())
+        comps["intra_n4"] = (lambda q=q, k=k, v=v, o=o: hd.hd_sfa_fwd(q, k, v, o, I.n, 0), fl, by)
+    if want("intra_n1"):
+        q1, k1, v1 = synth.qkv(I1.B, I1.L, I1.n, I1.Hq, I1.Hkv, I1.d, I1.dtype, dev)
+        o1 = torch.empty_like(q1)
+        fl = synth.useful_flops(I1.B, I1.L, I1.n, I1.Hq, I1.d, 0)
+        by = 2 * (2 * q1.numel() + k1.numel() + v1.numel())
+        comps["intra_n1"] = (lambda: hd.hd_sfa_fwd(q1, k1, v1, o1, I1.n, 0), fl, by)
+    if want("cross_n4"):
+        qx, kx, vx = synth.qkv(X.B, X.L, X.n, X.Hq, X.Hkv, X.d, X.dtype, dev)
+        ox = torch.empty_like(qx)
+        fl = synth.useful_flops(X.B, X.L, X.n, X.Hq, X.d, 1)
+        by = 2 * (2 * qx.numel() + kx.numel() + vx.numel())
+        comps["cross_n4"] = (lambda: hd.hd_sfa_fwd(qx, kx, vx, ox, X.n, 1), fl, by)
+    if want("decode_intra") or want("decode_cross"):
+        T_cap = Dc.ctx + 8
+        dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)
+        dcl = torch.full((Dc.B,), Dc.ctx, dtype=torch.int32, device=dev)
+        do = torch.empty_like(dq)
+        ws = torch.empty(hd.hd_sfa_decode_workspace_bytes(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap),
+                         dtype=torch.uint8, device=dev)
+        # algorithmic bytes: cache read for ctx+1 tokens (the new row from
+        # k_new/v_new), q read, o written, new rows written to the cache
+        tok_bytes = Dc.n * Dc.Hkv * Dc.d * 2
+        by = 2 * (Dc.ctx * tok_bytes * Dc.B) + 2 * dq.numel() * 2 + 2 * dkn.numel() * 2 * 2
+        for mode, name in ((0, "decode_intra"), (1, "decode_cross")):
+            if want(name):
+                keys = (Dc.ctx + 1) if mode == 0 else None
+                g = Dc.Hq // Dc.Hkv
+                if mode == 0:
+                    pairs = Dc.B * Dc.n * Dc.Hq * keys
+                else:
+                    pairs = Dc.B * Dc.Hq * sum(Dc.ctx * Dc.n + s + 1 for s in range(Dc.n))
+                fl = 4.0 * Dc.d * pairs
+                comps[name] = (lambda mode=mode: hd.hd_sfa_decode(dq, dkn, dvn, dkc, dvc, dcl, do, mode, 0, 0.0, ws),
+                               fl, by)
+                del g
+    if want("embed"):
+        tabs = synth.tables(E["n"], E["V"], E["D"], E["dtype"], dev)
+        # 64 rotating id sets so rows come from HBM rather than the last-level cache
+        idsets = [synth.token_ids(E["B"], E["L"], E["V"], seed=1000 + r, device=dev) for r in range(64)]
+        eo = torch.empty((E["B"], E["n"] * E["L"], E["D"]), dtype=E["dtype"], device=dev)
+        ctr = [0]
+
+        def run_embed():
+            hd.hd_expand_embed(idsets[ctr[0] % 64], tabs, eo)
+            ctr[0] += 1
+
+        by = 2 * eo.numel() * 2 + E["B"] * E["L"] * 4
+        comps["embed"] = (run_embed, 0.0, by)
+    if args.long:
+        for cfg, name in ((synth.LONG_INTRA_W, "long_intra_w4096"), (synth.LONG_CROSS, "long_cross")):
+            if want(name):
+                ql, kl, vl = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+                ol = torch.empty_like(ql)
+                fl = synth.useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+                by = 2 * (2 * ql.numel() + kl.numel() + vl.numel())
+                comps[name] = (lambda ql=ql, kl=kl, vl=vl, ol=ol, cfg=cfg:
+                               hd.hd_sfa_fwd(ql, kl, vl, ol, cfg.n, cfg.mode, cfg.window), fl, by)
+    torch.cuda.synchronize()
+
+    timer = Timer()
+    for _ in range(args.warmup):
+        for name, (fn, _, _) in comps.items():
+            timer.run(name, fn)
+    timer.collect()
+    timer.ms = {}
+    torch.cuda.synchronize()
+    step_s = torch.cuda.Event(enable_timing=True)
+    step_e = torch.cuda.Event(enable_timing=True)
+    step_s.record()
+    for step in range(args.steps):
+        for name, (fn, _, _) in comps.items():
+            timer.run(name, fn)
+    step_e.record()
+    timer.collect()
+    total_ms = step_s.elapsed_time(step_e)
+    ms_per_step = total_ms / max(args.steps, 1)
+
+    report = {}
+    for name, (fn, fl, by) in comps.items():
+        t = float(np.mean(timer.ms[name]))
+        report[name] = {"ms": round(t, 4), "ms_min": round(float(np.min(timer.ms[name])), 4)}
+        if fl:
+            report[name]["TFLOP/s"] = round(fl / t / 1e9, 2)
+        report[name]["GB/s"] = round(by / t / 1e6, 1)
+
+    value = report.get("intra_n4", {}).get("TFLOP/s")
+    ratio = None
+    if "intra_n4" in report and "intra_n1" in report:
+        ratio = round(report["intra_n4"]["ms"] / report["intra_n1"]["ms"], 3)
+    roof = None
+    if "intra_n4" in report:
+        fl = comps["intra_n4"][1]
+        ach = fl / report["intra_n4"]["ms"] / 1e9
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "sfa_fwd_bf16_kernel<128>", "per_launch_flops": fl}
+    roof_dec = None
+    if "decode_intra" in report:
+        by = comps["decode_intra"][2]
+        ach = by / report["decode_intra"]["ms"] / 1e6
+        roof_dec = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": round(ach / PEAK_HBM_GBPS, 4), "per_launch_bytes": by,
+                    "kernels": "decode_partial_kernel<128,1> + decode_combine_kernel<128>"}
+
+    line = {
+        "metric": "stream-factorized attn TFLOP/s (useful) at n=4 + n4/n1 time ratio; decode GB/s",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "intra-stream prefill n=4 L=4096 (nL=16384) B=1 32q/8kv d=128 bf16, "
+                               "plus n=1 control, cross layer, B=64 ctx-8192 decode, 4x160000x7168 gather",
+                   "n": 4, "seq_len_tokens": 4096, "expanded_len": 16384, "batch": 1,
+                   "heads_q": 32, "heads_kv": 8, "head_dim": 128},
+        "n4_n1_time_ratio": ratio,
+        "decode_GBps": {m: report[m]["GB/s"] for m in ("decode_intra", "decode_cross") if m in report},
+        "components": report,
+        "roofline": roof,
+        "roofline_decode": roof_dec,
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(args.cpu_seconds),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * hd.h -- C ABI of the Stream-Factorized Attention library (libhd.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (WeLM blog "Hidden Decoding at Scale", section "Method Recap and
+ * New Designs"): every token x_i is expanded into n stream embeddings taken from
+ * n independent tables and interleaved along the sequence; attention over the
+ * n*L-long expanded sequence is either intra-stream (causal inside a stream,
+ * streams invisible to one another) or cross-stream (causal over all
+ * positions), optionally inside a sliding window; decoding keeps one KV cache
+ * per stream and processes the n streams of a new token in one pass.
+ *
+ * Conventions shared by every entry point
+ *   - Indices are 0-based: expanded position t = i*n + s for token i in [0,L)
+ *     and stream s in [0,n) (the pages' 1-based t = (i-1)n + k).
+ *   - Every tensor pointer is DEVICE memory owned by the caller, row-major and
+ *     dense, 16-byte aligned.  The library allocates no memory, keeps no
+ *     pointer after a call returns and holds no state between calls except a
+ *     thread-local error string.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns without synchronising; results
+ *     are deterministic (no atomics, fixed reduction orders).
+ *   - dtype HD_BF16: inputs and outputs bfloat16, products accumulated in
+ *     float32, softmax in float32, outputs rounded to nearest even once.
+ *     dtype HD_F32: float32 end to end.
+ *   - GQA: query head h reads kv head h / (Hq/Hkv).
+ *   - Softmax scale: `scale` if > 0, else 1/sqrt(d).
+ *
+ * Error behaviour: arguments are validated on the host before anything is
+ * enqueued.  HD_ERR_INVALID: a size < 1 (where >= 1 is required), Hq not a
+ * multiple of Hkv, window < 0, n above HD_MAX_STREAMS, a NULL or misaligned
+ * pointer, or a too-small workspace.  HD_ERR_UNSUPPORTED: a head dim other than
+ * 32, 64 or 128, an unknown dtype or mode, or a shape past a documented limit.
+ * HD_ERR_DEVICE: the HIP runtime reported an error at launch.  On any non-OK
+ * return nothing was launched by that call (except HD_ERR_DEVICE, where an
+ * earlier kernel of the same call may have been enqueued) and hd_last_error()
+ * describes the problem.  Token ids outside [0,V) and cache_len[b] >= T_cap are
+ * caller contract violations that the device code does not check.
+ */
+#ifndef HD_H
+#define HD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HD_OK = 0,
+    HD_ERR_INVALID = 1,
+    HD_ERR_UNSUPPORTED = 2,
+    HD_ERR_DEVICE = 3
+} hd_status;
+
+typedef enum { HD_MODE_INTRA = 0, HD_MODE_CROSS = 1 } hd_mode;
+typedef enum { HD_BF16 = 0, HD_F32 = 1 } hd_dtype;
+
+#define HD_MAX_STREAMS 16
+
+/*
+ * Multi-stream expansion ("Multi-Stream Expansion and Training Objective",
+ * equation S_t = E_k(x_i) at t = (i-1)n + k):
+ *     out[b][i*n + s][:] = tables[s][ids[b][i]][:]
+ * a bit-exact row copy.
+ *   ids     device int32 [B][L], each in [0, V)
+ *   tables  HOST array of n device pointers, table s is [V][D] of dtype dt
+ *   out     device [B][n*L][D] of dtype dt
+ * Requires B, L >= 1, 1 <= n <= HD_MAX_STREAMS, V >= 1, D >= 1.
+ */
+hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n,
+                          const void *const *tables, int64_t V, int D, hd_dtype dt,
+                          void *out, void *stream);
+
+/*
+ * Stream-Factorized Attention prefill ("Stream-Factorized Attention", index
+ * maps i(t) = ceil(t/n), s(t) = (t-1) mod n + 1, and Figure 2).  For every
+ * query row (b, t_q, h) with i_q = t_q/n, s_q = t_q%n:
+ *   mode HD_MODE_INTRA (mask c): keys t_k = j*n + s_q with j <= i_q, and
+ *        i_q - j < window when window > 0 (window counts tokens, incl. self);
+ *   mode HD_MODE_CROSS (mask a; mask b when window > 0): keys t_k <= t_q, and
+ *        t_q - t_k < n*window when window > 0;
+ *   o = softmax(scale * q.k over the visible keys) . v
+ *   q, o  [B][n*L][Hq][d]         k, v  [B][n*L][Hkv][d]     (dtype dt)
+ *   lse   optional float32 [B][Hq][n*L]: natural log of the softmax
+ *         denominator sum_k exp(scale*q.k) over the visible keys (NULL = skip)
+ * Requires B, L, n, Hq, Hkv >= 1, Hq % Hkv == 0, d in {32, 64, 128},
+ * window >= 0, n <= HD_MAX_STREAMS, n*L <= 2^30.
+ */
+hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int B, int L, int n, int Hq, int Hkv, int d,
+                     hd_mode mode, int window, float scale, hd_dtype dt, void *stream);
+
+/*
+ * Bytes of device workspace hd_sfa_decode needs for these sizes (0 if the
+ * sizes are invalid).  The workspace holds float32 split-KV partial results.
+ */
+size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap);
+
+/*
+ * One decode step over the retained per-stream KV cache ("Persistent KV and
+ * the KV-mirror Saving": a separate KV cache per stream; "Inference
+ * Throughput": the n streams of the new token are processed in one pass).
+ * For sequence b with len = cache_len[b] tokens already cached:
+ *   1. the new token's keys/values are appended at token len:
+ *        k_cache[b][len][s][h][:] = k_new[b][s][h][:]   (same for v)
+ *   2. the query of stream s sits at expanded position t_q = len*n + s and
+ *      attends, under the layer's mask (see hd_sfa_fwd), over the keys of
+ *      tokens 0..len (the appended row included):
+ *        o[b][s][h][:] = softmax(scale * q.k) . v
+ *   q, o         [B][n][Hq][d]
+ *   k_new, v_new [B][n][Hkv][d]
+ *   k_cache, v_cache [B][T_cap][n][Hkv][d], rows >= len are never read
+ *   cache_len    DEVICE int32 [B], each in [0, T_cap); not modified (the
+ *                caller advances it after the step)
+ *   workspace    device, >= hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap)
+ *                bytes (HD_BF16; the HD_F32 path uses none and accepts NULL);
+ *                its contents on entry do not matter
+ * Requires the prefill size rules plus T_cap >= 1, n*(Hq/Hkv) <= 64.
+ */
+hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new,
+                        void *k_cache, void *v_cache, const int32_t *cache_len, int T_cap,
+                        void *o, int B, int n, int Hq, int Hkv, int d,
+                        hd_mode mode, int window, float scale, hd_dtype dt,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static name of a status code. */
+const char *hd_status_string(hd_status s);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char *hd_last_error(void);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int hd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HD_H */

@@ -1,0 +1,173 @@
+// api.hip -- the C ABI of libhd.so (declared in include/hd.h): argument
+// validation on the host, then dispatch to the HIP kernels on the caller's
+// stream.  No allocation, no synchronisation, no state beyond a thread-local
+// error string.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "hd.h"
+#include "hd_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hd_status fail(hd_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+hd_status ok() {
+    g_err[0] = '\0';
+    return HD_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hd_status check_ptr(const void *p, const char *name) {
+    if (p == nullptr) return fail(HD_ERR_INVALID, "%s is NULL", name);
+    if (!aligned16(p)) return fail(HD_ERR_INVALID, "%s is not 16-byte aligned", name);
+    return HD_OK;
+}
+
+hd_status device_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(HD_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HD_TRY(expr)                         \
+    do {                                     \
+        hd_status _s = (expr);               \
+        if (_s != HD_OK) return _s;          \
+    } while (0)
+
+// Shared validation of the attention sizes.
+hd_status check_attn(int B, int n, int Hq, int Hkv, int d, int mode, int window, hd_dtype dt) {
+    if (B < 1 || n < 1 || Hq < 1 || Hkv < 1)
+        return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d n=%d Hq=%d Hkv=%d)", B, n, Hq, Hkv);
+    if (n > HD_MAX_STREAMS) return fail(HD_ERR_INVALID, "n=%d above HD_MAX_STREAMS=%d", n, HD_MAX_STREAMS);
+    if (Hq % Hkv) return fail(HD_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    if (window < 0) return fail(HD_ERR_INVALID, "window=%d < 0", window);
+    if (d != 32 && d != 64 && d != 128) return fail(HD_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (mode != HD_MODE_INTRA && mode != HD_MODE_CROSS) return fail(HD_ERR_UNSUPPORTED, "unknown mode %d", mode);
+    return HD_OK;
+}
+
+float resolve_scale(float scale, int d) {
+    return (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt((float)d);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hd_status_string(hd_status s) {
+    switch (s) {
+        case HD_OK: return "HD_OK";
+        case HD_ERR_INVALID: return "HD_ERR_INVALID";
+        case HD_ERR_UNSUPPORTED: return "HD_ERR_UNSUPPORTED";
+        case HD_ERR_DEVICE: return "HD_ERR_DEVICE";
+    }
+    return "HD_ERR_UNKNOWN";
+}
+
+const char *hd_last_error(void) { return g_err; }
+
+int hd_version(void) { return 100; }
+
+hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n, const void *const *tables, int64_t V,
+                          int D, hd_dtype dt, void *out, void *stream) {
+    if (B < 1 || L < 1 || n < 1 || V < 1 || D < 1)
+        return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d L=%d n=%d V=%lld D=%d)", B, L, n, (long long)V, D);
+    if (n > HD_MAX_STREAMS) return fail(HD_ERR_INVALID, "n=%d above HD_MAX_STREAMS=%d", n, HD_MAX_STREAMS);
+    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (tables == nullptr) return fail(HD_ERR_INVALID, "tables is NULL");
+    HD_TRY(check_ptr(ids, "ids"));
+    HD_TRY(check_ptr(out, "out"));
+    hd::EmbedArgs a{};
+    for (int s = 0; s < n; ++s) {
+        HD_TRY(check_ptr(tables[s], "tables[s]"));
+        a.tables[s] = static_cast<const char *>(tables[s]);
+    }
+    a.ids = ids;
+    a.out = static_cast<char *>(out);
+    a.B = B;
+    a.L = L;
+    a.n = n;
+    a.row_bytes = (int64_t)D * (dt == HD_BF16 ? 2 : 4);
+    return device_status(hd::launch_expand_embed(a, static_cast<hipStream_t>(stream)), "expand_embed launch");
+}
+
+hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int L, int n,
+                     int Hq, int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt, void *stream) {
+    if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
+    HD_TRY(check_ptr(q, "q"));
+    HD_TRY(check_ptr(k, "k"));
+    HD_TRY(check_ptr(v, "v"));
+    HD_TRY(check_ptr(o, "o"));
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
+    hd::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    if (mode == HD_MODE_INTRA) {
+        a.Lsub = L; a.nsub = n; a.stride = n;
+        a.weff = window;
+    } else {
+        a.Lsub = n * L; a.nsub = 1; a.stride = 1;
+        const int64_t w = (int64_t)n * window;
+        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
+    }
+    if (mode == HD_MODE_INTRA && window >= L) a.weff = 0;  // window covers everything
+    a.scale = resolve_scale(scale, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
+    return device_status(e, "sfa_fwd launch");
+}
+
+size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap) {
+    if (B < 1 || n < 1 || Hq < 1 || Hkv < 1 || d < 1 || T_cap < 1 || Hq % Hkv) return 0;
+    return hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);
+}
+
+hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                        const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                        hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    if (T_cap < 1) return fail(HD_ERR_INVALID, "T_cap=%d < 1", T_cap);
+    if (n * (Hq / Hkv) > 64)
+        return fail(HD_ERR_UNSUPPORTED, "n*(Hq/Hkv)=%d query rows per kv head above 64", n * (Hq / Hkv));
+    HD_TRY(check_ptr(q, "q"));
+    HD_TRY(check_ptr(k_new, "k_new"));
+    HD_TRY(check_ptr(v_new, "v_new"));
+    HD_TRY(check_ptr(k_cache, "k_cache"));
+    HD_TRY(check_ptr(v_cache, "v_cache"));
+    HD_TRY(check_ptr(cache_len, "cache_len"));
+    HD_TRY(check_ptr(o, "o"));
+    hd::DecArgs a{};
+    a.q = q; a.k_new = k_new; a.v_new = v_new; a.k_cache = k_cache; a.v_cache = v_cache;
+    a.cache_len = cache_len; a.o = o;
+    a.B = B; a.n = n; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.T_cap = T_cap;
+    a.mode = (int)mode; a.window = window;
+    a.scale = resolve_scale(scale, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (dt == HD_BF16) {
+        const size_t need = hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);
+        if (workspace_bytes < need)
+            return fail(HD_ERR_INVALID, "workspace of %zu bytes below the %zu required", workspace_bytes, need);
+        HD_TRY(check_ptr(workspace, "workspace"));
+        a.ws = static_cast<float *>(workspace);
+        return device_status(hd::launch_sfa_decode_bf16(a, st), "sfa_decode launch");
+    }
+    return device_status(hd::launch_sfa_decode_f32(a, st), "sfa_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// hd_internal.h -- types and launcher declarations shared by the HIP sources
+// of libhd.so.  Not part of the public ABI (that is include/hd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// Expansion: out[b][i*n+s][:] = tables[s][ids[b][i]][:]
+struct EmbedArgs {
+    const int32_t *ids;
+    const char *tables[16];
+    char *out;
+    int B, L, n;
+    int64_t row_bytes;
+};
+hipError_t launch_expand_embed(const EmbedArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Prefill.  Both masks are run as causal attention over a strided
+// "sub-sequence" of the expanded sequence:
+//   intra: one sub-sequence per stream s, element j at position j*n + s,
+//          length L, window W tokens;
+//   cross: one sub-sequence (the whole expanded sequence), element j at
+//          position j, length n*L, window n*W positions.
+// A key j is visible to query i of the same sub-sequence iff
+//   j <= i  and  (weff == 0 || i - j < weff).
+struct FwdArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, nL, Hq, Hkv, d;
+    int Lsub;     // elements per sub-sequence
+    int nsub;     // sub-sequences per batch row (n for intra, 1 for cross)
+    int stride;   // expanded positions between consecutive elements
+    int weff;     // window in sub-sequence elements, 0 = none
+    float scale;  // softmax scale (already resolved, > 0)
+};
+hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st);
+hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Decode over the per-stream cache [B][T_cap][n][Hkv][d].
+struct DecArgs {
+    const void *q, *k_new, *v_new;
+    void *k_cache, *v_cache;
+    const int32_t *cache_len;
+    void *o;
+    float *ws;          // split-KV partials (bf16 path)
+    int B, n, Hq, Hkv, d, T_cap;
+    int mode;           // 0 intra, 1 cross
+    int window;         // tokens, 0 = none
+    float scale;
+};
+size_t decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap);
+hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st);
+hipError_t launch_sfa_decode_f32(const DecArgs &a, hipStream_t st);
+
+}  // namespace hd

@@ -1,0 +1,369 @@
+// sfa_decode_bf16.hip -- one decode step of Stream-Factorized Attention over
+// the retained per-stream KV cache, bf16 in / fp32 accumulate.
+//
+// Method ("Hidden Decoding at Scale"): one KV cache per stream is kept
+// ("Persistent KV and the KV-mirror Saving") and the n streams of the new
+// token are processed together in one pass ("Inference Throughput").  The new
+// token's query of stream s sits at expanded position len*n + s and attends
+// under the layer's mask (Figure 2) over tokens 0..len.
+//
+// The step is HBM-bound: the cache is read once.  It runs as split-KV:
+//   kernel 1  grid (split, b*Hkv): a workgroup streams `chunk` tokens x n
+//             streams of one kv head's cache and scores them against all
+//             n*g queries of that head group (g = Hq/Hkv) at once -- 16-row
+//             query blocks on v_mfma_f32_16x16x32_bf16 -- then merges its four
+//             waves and writes one fp32 partial (max, sum, acc[d]) per query.
+//             The split holding token len also appends the new K/V rows to
+//             the cache; no split reads cache row len (the new row is read
+//             from k_new / v_new), so the append races with nothing.
+//   kernel 2  one wavefront per output row merges the partials of the splits
+//             that ran, in split order (log-sum-exp), and rounds to bf16.
+// Intra-stream layers use only the stream-diagonal entries of each score
+// block; the masked lanes cost matrix-core cycles, not bytes.
+//
+// 16x16x32 bf16 operand layout: lane l supplies row (l % 16) of A / column of
+// B and k-slots 8*(l/16) .. +7; the accumulator holds C[4*(l/16) + i][l % 16].
+#include "hd_internal.h"
+
+namespace hd {
+
+namespace {
+
+constexpr int NW = 4;    // waves per workgroup
+constexpr int RB = 32;   // cache rows per wave block
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split {
+    int chunk;   // tokens per split
+    int nsplit;  // splits per (b, kv head)
+};
+
+Split choose_split(int B, int Hkv, int T_cap) {
+    // Aim for at least ~2048 workgroups (8 per CU) so enough cache bytes are in
+    // flight, with chunks of >= 64 tokens and a multiple of 16 tokens.
+    const int64_t bh = (int64_t)B * Hkv;
+    int64_t want = (2048 + bh - 1) / bh;
+    int64_t chunk = ((int64_t)T_cap + want - 1) / want;
+    chunk = ((chunk + 15) / 16) * 16;
+    if (chunk < 64) chunk = 64;
+    Split s;
+    s.chunk = (int)chunk;
+    s.nsplit = (int)(((int64_t)T_cap + chunk - 1) / chunk);
+    return s;
+}
+
+template <int D, int NQB>
+__global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp, float scale_log2) {
+    constexpr int VP = D + 8;  // LDS pitch of the staged V rows
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x;
+    const int bh = blockIdx.y;
+    const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
+    const int n = p.n, g = p.Hq / p.Hkv, QR = n * g;
+    const int len = p.cache_len[b];
+    const int c0 = split * sp.chunk;
+    if (c0 > len) return;  // nothing cached here yet; the combine skips it
+    const int c1 = min(c0 + sp.chunk, len + 1);
+
+    const bf16 *kn = static_cast<const bf16 *>(p.k_new);
+    const bf16 *vn = static_cast<const bf16 *>(p.v_new);
+    bf16 *kc = static_cast<bf16 *>(p.k_cache);
+    bf16 *vc = static_cast<bf16 *>(p.v_cache);
+    const int64_t cache_tok = (int64_t)n * p.Hkv * D;  // elements per cached token
+    const int64_t cache_b = (int64_t)b * p.T_cap * cache_tok + (int64_t)kvh * D;
+    const int64_t new_b = (int64_t)b * n * p.Hkv * D + (int64_t)kvh * D;
+
+    // Append the new token's rows of this kv head (row len is read by nobody).
+    if (len < c1) {
+        for (int c = tid; c < n * (D / 8); c += 256) {
+            const int s = c / (D / 8), cc = c - s * (D / 8);
+            const int64_t src = new_b + (int64_t)s * p.Hkv * D + cc * 8;
+            const int64_t dst = cache_b + (int64_t)len * cache_tok + (int64_t)s * p.Hkv * D + cc * 8;
+            *reinterpret_cast<uint4 *>(kc + dst) = *reinterpret_cast<const uint4 *>(kn + src);
+            *reinterpret_cast<uint4 *>(vc + dst) = *reinterpret_cast<const uint4 *>(vn + src);
+        }
+    }
+
+    // Tokens older than len - window are invisible to every query.
+    const int tlo = p.window ? max(c0, len - p.window) : c0;
+    const int64_t row_lo = (int64_t)tlo * n, row_hi = (int64_t)c1 * n;
+    const int nrow = row_hi > row_lo ? (int)(row_hi - row_lo) : 0;
+    const int nblk = (nrow + RB - 1) / RB;
+    const int iters = (nblk + NW - 1) / NW;
+
+    // Query operands: block qb, lane column l16 is query row c = qb*16 + l16
+    // (row c <-> stream c / g, head kvh*g + c % g); slots grp hold dims
+    // ks*32 + 8*grp .. +7.
+    const bf16 *qg = static_cast<const bf16 *>(p.q);
+    bf16x8 qop[NQB][D / 32];
+    int qstream[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int c = qb * 16 + l16;
+        const bool ok = c < QR;
+        const int s = ok ? c / g : 0, hh = ok ? c - s * g : 0;
+        qstream[qb] = s;
+        const bf16 *qp = qg + (((int64_t)b * n + s) * p.Hq + kvh * g + hh) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 32);
+            qop[qb][ks] = ok ? x : bf16x8{};
+        }
+    }
+
+    f32x4 oacc[NQB][D / 16];
+    float m_run[NQB], l_run[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) oacc[qb][db] = f32x4{};
+    }
+
+    bf16 *Vw = reinterpret_cast<bf16 *>(smem) + wave * RB * VP;
+    const int64_t tq_base = (int64_t)len * n;
+
+    for (int it = 0; it < iters; ++it) {
+        const int blk = it * NW + wave;
+        const int64_t rbase = row_lo + (int64_t)blk * RB;
+
+        // Source address of cache row r (token r/n, stream r%n); -1 if absent.
+        auto row_src = [&](int64_t r, const bf16 *&kp, const bf16 *&vp) -> bool {
+            if (blk >= nblk || r >= row_hi) return false;
+            const int64_t tok = r / n;
+            const int s = (int)(r - tok * n);
+            if (tok < len) {
+                const int64_t off = cache_b + tok * cache_tok + (int64_t)s * p.Hkv * D;
+                kp = kc + off; vp = vc + off;
+            } else {
+                const int64_t off = new_b + (int64_t)s * p.Hkv * D;
+                kp = kn + off; vp = vn + off;
+            }
+            return true;
+        };
+
+        // K operands straight from global memory, V rows into this wave's LDS.
+        bf16x8 kop[2][D / 32];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const bf16 *kp = nullptr, *vp = nullptr;
+            const bool ok = row_src(rbase + kh * 16 + l16, kp, vp);
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks)
+                kop[kh][ks] = ok ? *reinterpret_cast<const bf16x8 *>(kp + ks * 32 + 8 * grp) : bf16x8{};
+        }
+#pragma unroll
+        for (int c = lane; c < RB * (D / 8); c += 64) {
+            const int r = c / (D / 8), cc = c - r * (D / 8);
+            const bf16 *kp = nullptr, *vp = nullptr;
+            uint4 x = {0, 0, 0, 0};
+            if (row_src(rbase + r, kp, vp)) x = *reinterpret_cast<const uint4 *>(vp + cc * 8);
+            *reinterpret_cast<uint4 *>(Vw + r * VP + cc * 8) = x;
+        }
+        __syncthreads();
+
+        if (blk < nblk) {
+#pragma unroll
+            for (int qb = 0; qb < NQB; ++qb) {
+                f32x4 sacc[2];
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    sacc[kh] = f32x4{};
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks) sacc[kh] = mfma16(kop[kh][ks], qop[qb][ks], sacc[kh]);
+                }
+                const int sq = qstream[qb];
+                const int64_t tq = tq_base + sq;
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t r = rbase + kh * 16 + 4 * grp + i;
+                        const int64_t tok = r / n;
+                        const int sk = (int)(r - tok * n);
+                        bool vis = r < row_hi;
+                        if (p.mode == 0) vis = vis && sk == sq && (p.window == 0 || len - tok < p.window);
+                        else vis = vis && r <= tq && (p.window == 0 || tq - r < (int64_t)n * p.window);
+                        const float x = vis ? sacc[kh][i] * scale_log2 : -INFINITY;
+                        sacc[kh][i] = x;
+                        mx = fmaxf(mx, x);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                const float m_new = fmaxf(m_run[qb], mx);
+                const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+                const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_use);
+                bf16x8 pop;
+                float lsum = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float pv = __builtin_amdgcn_exp2f(sacc[j >> 2][j & 3] - m_use);
+                    lsum += pv;
+                    pop[j] = (bf16)pv;
+                }
+                l_run[qb] = l_run[qb] * alpha + lsum;
+                m_run[qb] = m_new;
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) oacc[qb][db] *= alpha;
+                // slot j <-> key row 16*(j/4) + 4*grp + (j%4) of the block
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) {
+                    bf16x8 vop;
+                    const bf16 *vcol = Vw + 4 * grp * VP + db * 16 + l16;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) vop[j] = vcol[(16 * (j >> 2) + (j & 3)) * VP];
+                    oacc[qb][db] = mfma16(vop, pop, oacc[qb][db]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // Merge the four waves, then write this split's partial per query row.
+    float *ml = reinterpret_cast<float *>(smem);            // [NW][NQB*16][2]
+    float *ow = ml + NW * NQB * 16 * 2;                     // [NW][NQB*16][D]
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        float lt = l_run[qb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int c = qb * 16 + l16;
+        if (grp == 0) {
+            ml[(wave * NQB * 16 + c) * 2 + 0] = m_run[qb];
+            ml[(wave * NQB * 16 + c) * 2 + 1] = lt;
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ow[(wave * NQB * 16 + c) * D + db * 16 + 4 * grp + i] = oacc[qb][db][i];
+    }
+    __syncthreads();
+    const int64_t part = ((int64_t)bh * sp.nsplit + split) * QR;
+    float *ws_acc = p.ws;
+    float *ws_ml = p.ws + (int64_t)p.B * p.Hkv * sp.nsplit * QR * D;
+    for (int e = tid; e < QR * D; e += 256) {
+        const int c = e / D, dim = e - c * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[(w * NQB * 16 + c) * 2]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(ml[(w * NQB * 16 + c) * 2] - Mu);
+            acc += wt * ow[(w * NQB * 16 + c) * D + dim];
+            L += wt * ml[(w * NQB * 16 + c) * 2 + 1];
+        }
+        ws_acc[(part + c) * D + dim] = acc;
+        if (dim == 0) {
+            ws_ml[(part + c) * 2 + 0] = M;
+            ws_ml[(part + c) * 2 + 1] = L;
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp) {
+    const int lane = threadIdx.x & 63;
+    const int g = p.Hq / p.Hkv, QR = p.n * g;
+    const int64_t row = (int64_t)blockIdx.x * NW + (threadIdx.x >> 6);  // (bh, c)
+    if (row >= (int64_t)p.B * p.Hkv * QR) return;
+    const int c = (int)(row % QR);
+    const int bh = (int)(row / QR);
+    const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
+    const int len = p.cache_len[b];
+    const int ns = min(sp.nsplit, len / sp.chunk + 1);  // splits with c0 <= len
+    const float *ws_acc = p.ws;
+    const float *ws_ml = p.ws + (int64_t)p.B * p.Hkv * sp.nsplit * QR * D;
+    const int64_t part0 = (int64_t)bh * sp.nsplit * QR + c;
+
+    float M = -INFINITY;
+    for (int k = 0; k < ns; ++k) M = fmaxf(M, ws_ml[(part0 + (int64_t)k * QR) * 2]);
+    constexpr int PER = (D + 63) / 64;
+    float acc[PER] = {};
+    float L = 0.f;
+    for (int k = 0; k < ns; ++k) {
+        const int64_t pk = part0 + (int64_t)k * QR;
+        const float wt = __builtin_amdgcn_exp2f(ws_ml[pk * 2] - M);
+        L += wt * ws_ml[pk * 2 + 1];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int dim = lane + 64 * e;
+            if (dim < D) acc[e] += wt * ws_acc[pk * D + dim];
+        }
+    }
+    const int s = c / g, hh = c - s * g;
+    bf16 *op = static_cast<bf16 *>(p.o) + (((int64_t)b * p.n + s) * p.Hq + kvh * g + hh) * D;
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int dim = lane + 64 * e;
+        if (dim < D) op[dim] = (bf16)(acc[e] * inv);
+    }
+}
+
+template <int D, int NQB>
+hipError_t launch_partial(const DecArgs &a, Split sp, float sl2, hipStream_t st) {
+    constexpr int VP = D + 8;
+    const size_t stage = (size_t)NW * RB * VP * sizeof(bf16);
+    const size_t merge = (size_t)NW * NQB * 16 * (2 + D) * sizeof(float);
+    const size_t lds = stage > merge ? stage : merge;
+    if (lds > 65536) {  // above the default dynamic-LDS limit: opt in once
+        static bool raised = false;
+        if (!raised) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&decode_partial_kernel<D, NQB>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    hipLaunchKernelGGL((decode_partial_kernel<D, NQB>), dim3(sp.nsplit, a.B * a.Hkv), dim3(256), lds, st, a,
+                       sp, sl2);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const DecArgs &a, Split sp, float sl2, hipStream_t st) {
+    const int QR = a.n * (a.Hq / a.Hkv);
+    hipError_t e;
+    switch ((QR + 15) / 16) {
+        case 1: e = launch_partial<D, 1>(a, sp, sl2, st); break;
+        case 2: e = launch_partial<D, 2>(a, sp, sl2, st); break;
+        case 3: e = launch_partial<D, 3>(a, sp, sl2, st); break;
+        case 4: e = launch_partial<D, 4>(a, sp, sl2, st); break;
+        default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)a.B * a.Hkv * QR;
+    hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((unsigned)((rows + NW - 1) / NW)), dim3(256), 0, st, a, sp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap) {
+    const Split sp = choose_split(B, Hkv, T_cap);
+    return (size_t)B * n * Hq * sp.nsplit * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st) {
+    const Split sp = choose_split(a.B, a.Hkv, a.T_cap);
+    const float sl2 = a.scale * kLog2e;
+    switch (a.d) {
+        case 32: return launch_d<32>(a, sp, sl2, st);
+        case 64: return launch_d<64>(a, sp, sl2, st);
+        case 128: return launch_d<128>(a, sp, sl2, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hd

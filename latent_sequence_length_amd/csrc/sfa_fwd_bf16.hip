@@ -1,0 +1,240 @@
+// sfa_fwd_bf16.hip -- Stream-Factorized Attention prefill, bf16 in / fp32
+// accumulate, on gfx950 matrix cores.
+//
+// The method ("Hidden Decoding at Scale", "Stream-Factorized Attention",
+// Figure 2): intra-stream layers attend causally within a stream only, cross-
+// stream layers causally over the whole expanded sequence, each optionally in
+// a sliding window.  Both are run here as causal attention over a strided
+// sub-sequence (see FwdArgs): for intra, the keys of stream s are rows
+// s, s+n, s+2n, ... of K/V, gathered by address arithmetic into LDS tiles, so
+// no mask tensor exists and no tile of another stream is ever loaded.
+//
+// Work decomposition
+//   workgroup = 4 wavefronts = one kv head, HG query heads of its GQA group x
+//               TB blocks of 32 consecutive sub-sequence queries (HG*TB = 4);
+//               the K/V tile in LDS is shared by all four waves.
+//   wave      = 32 queries of one head.
+//   tile      = 64 keys.
+// Per tile each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (two
+// 32-key blocks), so lane l owns query (l % 32) and 16 keys of each block: the
+// online-softmax row state (max, sum) lives in one lane pair (l, l^32).  Then
+// O^T += V^T P^T with the same instruction; P^T comes straight out of the S^T
+// accumulator registers (no LDS round trip) and O^T keeps every accumulator
+// of a lane on that lane's own query, so the rescale is one scalar per lane.
+//
+// Operand layouts of the 32x32x16 bf16 instruction used below: lane l supplies
+// row (l % 32) of A (column of B) and eight consecutive k-slots of half
+// (l / 32); A and B pair k-slots identically, so any consistent assignment of
+// real k indices to slots is a valid contraction.  The accumulator holds
+// C[8*(r/4) + 4*(l/32) + (r%4)][l % 32] in register r.
+#include "hd_internal.h"
+
+namespace hd {
+
+namespace {
+
+constexpr int KT = 64;   // keys per tile
+constexpr int QW = 32;   // queries per wave
+constexpr int NWAVE = 4;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_xor32(float x) {
+    return __shfl_xor(x, 32, 64);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, int TB, int nqblk,
+                                                           float scale_log2) {
+    constexpr int KP = D + 8;  // LDS row pitch (elements): 16-byte pad per row
+    __shared__ __attribute__((aligned(16))) bf16 Ks[KT * KP];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[KT * KP];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int g = p.Hq / p.Hkv, ngrp = g / HG;
+
+    // Workgroup -> (q block, b, kv head, head group, sub-sequence).  The last
+    // (longest) query blocks are dispatched first.
+    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
+    const int qblk = nqblk - 1 - (int)(blockIdx.x / nrest);
+    int rest = (int)(blockIdx.x % nrest);
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int hgrp = rest % ngrp; rest /= ngrp;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+
+    const int QB = QW * TB;
+    const int q0 = qblk * QB;
+    const int hw = wave % HG, tb = wave / HG;
+    const int h = kvh * g + hgrp * HG + hw;
+    const int qw0 = q0 + tb * QW;       // first query of this wave
+    const int myq = qw0 + l32;          // this lane's query (sub-sequence index)
+    const bool qvalid = myq < p.Lsub;
+
+    const int64_t qrs = (int64_t)p.Hq * D;   // elements between positions (Q, O)
+    const int64_t krs = (int64_t)p.Hkv * D;  // elements between positions (K, V)
+    const int64_t bpos = (int64_t)b * p.nL + sub;
+    const bf16 *qg = static_cast<const bf16 *>(p.q);
+    const bf16 *kg = static_cast<const bf16 *>(p.k);
+    const bf16 *vg = static_cast<const bf16 *>(p.v);
+
+    // Q^T operand, resident for the whole loop: slot half hi of k-step ks
+    // holds dims ks*16 + 8*hi .. +7 of this lane's query.
+    bf16x8 qop[D / 16];
+    {
+        const bf16 *qp = qg + (bpos + (int64_t)(qvalid ? myq : 0) * p.stride) * qrs + (int64_t)h * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
+            qop[ks] = qvalid ? x : bf16x8{};
+        }
+    }
+
+    f32x16 oacc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    const int kend = min(q0 + QB, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    constexpr int CH = D / 8;  // 16-byte chunks per row
+
+    for (int t0 = kbeg & ~(KT - 1); t0 < kend; t0 += KT) {
+        __syncthreads();  // previous tile fully consumed
+        for (int c = tid; c < KT * CH; c += 256) {
+            const int r = c / CH, cc = c - r * CH;
+            const int j = t0 + r;
+            uint4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
+            if (j < p.Lsub) {
+                const int64_t off = (bpos + (int64_t)j * p.stride) * krs + (int64_t)kvh * D + cc * 8;
+                kx = *reinterpret_cast<const uint4 *>(kg + off);
+                vx = *reinterpret_cast<const uint4 *>(vg + off);
+            }
+            *reinterpret_cast<uint4 *>(&Ks[r * KP + cc * 8]) = kx;
+            *reinterpret_cast<uint4 *>(&Vs[r * KP + cc * 8]) = vx;
+        }
+        __syncthreads();
+
+        // Skip tiles wholly outside this wave's causal / window band.
+        const bool active = (t0 <= qw0 + QW - 1) && (p.weff == 0 || t0 + KT - 1 > qw0 - p.weff);
+        if (!active) continue;
+        const bool need_mask = (t0 + KT - 1 > qw0) || (t0 + KT > p.Lsub) ||
+                               (p.weff != 0 && t0 <= qw0 + QW - 1 - p.weff);
+
+        // S^T = K Q^T for two 32-key blocks.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sacc[kb] = f32x16{};
+            const bf16 *kr = &Ks[(kb * 32 + l32) * KP + 8 * hi];
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks)
+                sacc[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kr + ks * 16), qop[ks], sacc[kb]);
+        }
+
+        // Scale to log2 units, mask, tile max.
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = sacc[kb][r] * scale_log2;
+                if (need_mask) {
+                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    const bool vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                    x = vis ? x : -INFINITY;
+                }
+                sacc[kb][r] = x;
+                mx = fmaxf(mx, x);
+            }
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float pv = __builtin_amdgcn_exp2f(sacc[kb][r] - m_use);
+                sacc[kb][r] = pv;
+                lsum += pv;
+            }
+        l_run = l_run * alpha + lsum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+
+        // O^T += V^T P^T.  PV step (kb, m2) contracts the 16 keys held in
+        // registers 8*m2 .. 8*m2+7 of block kb: slot j <-> key
+        // kb*32 + 16*m2 + 8*(j/4) + 4*hi + (j%4).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                bf16x8 pop;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) pop[j] = (bf16)sacc[kb][8 * m2 + j];
+                const int kbase = kb * 32 + 16 * m2 + 4 * hi;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    bf16x8 vop;
+                    const bf16 *vc = &Vs[db * 32 + l32];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) vop[j] = vc[(kbase + 8 * (j >> 2) + (j & 3)) * KP];
+                    oacc[db] = mfma32(vop, pop, oacc[db]);
+                }
+            }
+    }
+
+    // Epilogue: combine the lane pair's partial sums, normalise, store.
+    const float l_tot = l_run + wave_xor32(l_run);
+    if (qvalid) {
+        const float inv = 1.f / l_tot;
+        const int64_t pos = bpos + (int64_t)myq * p.stride;
+        bf16 *op = static_cast<bf16 *>(p.o) + pos * qrs + (int64_t)h * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                bf16x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[db][4 * r4 + e] * inv);
+                *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * r4 + 4 * hi) = y;
+            }
+        if (p.lse != nullptr && hi == 0)
+            p.lse[((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL)] =
+                m_run * kLn2 + __logf(l_tot);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
+    const int g = a.Hq / a.Hkv;
+    const int HG = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+    const int TB = NWAVE / HG;
+    const int nqblk = (a.Lsub + QW * TB - 1) / (QW * TB);
+    const int64_t grid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const float sl2 = a.scale * kLog2e;
+    switch (a.d) {
+        case 32:
+            hipLaunchKernelGGL(sfa_fwd_bf16_kernel<32>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
+            break;
+        case 64:
+            hipLaunchKernelGGL(sfa_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
+            break;
+        case 128:
+            hipLaunchKernelGGL(sfa_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hd

@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: libhd.so loads, exports every symbol that
+include/hd.h declares, and rejects bad arguments on the host before any HIP
+call (every call below fails validation, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from latent_sequence_length_amd import hd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from latent_sequence_length_amd import build
+
+    srcs = build.sources()
+    if not os.path.exists(hd.LIB_PATH) or os.path.getmtime(hd.LIB_PATH) < max(
+            os.path.getmtime(s) for s in srcs + [HEADER]):
+        build.build()
+    return hd.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_symbols() == sorted([
+        "hd_expand_embed", "hd_sfa_fwd", "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
+        "hd_status_string", "hd_last_error", "hd_version"])
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = os.popen(f"nm -D --defined-only {hd.LIB_PATH}").read()
+    for name in declared_symbols():
+        assert re.search(rf"\bT {name}$", out, re.M), name
+
+
+def test_status_strings(lib):
+    assert [hd.status_string(s) for s in range(4)] == [
+        "HD_OK", "HD_ERR_INVALID", "HD_ERR_UNSUPPORTED", "HD_ERR_DEVICE"]
+    assert lib.hd_version() >= 100
+
+
+FAKE = 0x10000  # aligned non-null address; never dereferenced (validation fails first)
+
+
+def fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, L=8, n=2, Hq=4, Hkv=2, d=64,
+             mode=0, window=0, scale=0.0, dt=0, stream=None)
+    a.update(kw)
+    return lib.hd_sfa_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), hd.HD_ERR_INVALID), (dict(L=0), hd.HD_ERR_INVALID), (dict(n=0), hd.HD_ERR_INVALID),
+    (dict(n=17), hd.HD_ERR_INVALID), (dict(Hq=3), hd.HD_ERR_INVALID), (dict(Hkv=0), hd.HD_ERR_INVALID),
+    (dict(window=-1), hd.HD_ERR_INVALID), (dict(q=None), hd.HD_ERR_INVALID),
+    (dict(k=FAKE + 8), hd.HD_ERR_INVALID), (dict(o=None), hd.HD_ERR_INVALID),
+    (dict(lse=FAKE + 2), hd.HD_ERR_INVALID),
+    (dict(d=96), hd.HD_ERR_UNSUPPORTED), (dict(d=16), hd.HD_ERR_UNSUPPORTED),
+    (dict(dt=7), hd.HD_ERR_UNSUPPORTED), (dict(mode=2), hd.HD_ERR_UNSUPPORTED),
+    (dict(L=1 << 29, n=4), hd.HD_ERR_UNSUPPORTED),
+])
+def test_fwd_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+    assert hd.last_error() != ""
+
+
+def dec(lib, **kw):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, cache_len=FAKE, T_cap=16,
+             o=FAKE, B=2, n=4, Hq=8, Hkv=2, d=128, mode=1, window=0, scale=0.0, dt=0,
+             workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return lib.hd_sfa_decode(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T_cap=0), hd.HD_ERR_INVALID), (dict(B=0), hd.HD_ERR_INVALID), (dict(Hq=6, Hkv=4), hd.HD_ERR_INVALID),
+    (dict(cache_len=None), hd.HD_ERR_INVALID), (dict(k_cache=FAKE + 4), hd.HD_ERR_INVALID),
+    (dict(workspace_bytes=16), hd.HD_ERR_INVALID),  # too small for the bf16 path
+    (dict(n=8, Hq=32, Hkv=2), hd.HD_ERR_UNSUPPORTED),  # 8*16 = 128 query rows per kv head
+    (dict(d=48), hd.HD_ERR_UNSUPPORTED), (dict(window=-3), hd.HD_ERR_INVALID),
+])
+def test_decode_validation(lib, kw, code):
+    assert dec(lib, **kw) == code
+
+
+def test_workspace_size_is_monotone_and_zero_on_bad_sizes(lib):
+    f = hd.hd_sfa_decode_workspace_bytes
+    assert f(0, 4, 32, 8, 128, 8193) == 0
+    assert f(64, 4, 30, 8, 128, 8193) == 0
+    a, b = f(64, 4, 32, 8, 128, 8193), f(64, 4, 32, 8, 128, 16385)
+    assert 0 < a <= b
+    # partials: B*n*Hq*(d+2) floats per split
+    assert a % (64 * 4 * 32 * 130 * 4) == 0
+
+
+def test_embed_validation(lib):
+    tabs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    f = lib.hd_expand_embed
+    assert f(FAKE, 0, 4, 2, tabs, 10, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+    assert f(FAKE, 1, 4, 0, tabs, 10, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+    assert f(FAKE, 1, 4, 2, None, 10, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+    assert f(FAKE, 1, 4, 2, tabs, 0, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+    assert f(FAKE, 1, 4, 2, tabs, 10, 8, 5, FAKE, None) == hd.HD_ERR_UNSUPPORTED
+    bad = (ctypes.c_void_p * 2)(FAKE, FAKE + 2)
+    assert f(FAKE, 1, 4, 2, bad, 10, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+    assert f(None, 1, 4, 2, tabs, 10, 8, 0, FAKE, None) == hd.HD_ERR_INVALID
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+
+    q = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        hd.sfa_fwd(q, q, q, 2, 0)

@@ -1,0 +1,296 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every input comes from the seeded generators in ``latent_sequence_length_amd.synth``;
+the oracle receives a host copy of the very same tensors.  Bars:
+  - expansion gather and decode cache append: bit-exact;
+  - bf16 attention: max |gpu - oracle| <= 2e-2 and mean <= 2e-3;
+  - float32 attention: max |gpu - oracle| <= 1e-4;
+  - lse: max abs <= 1e-3 (bf16 inputs; the scores are fp32 products of the
+    same bf16 values), 1e-4 (float32).
+Small shapes are compared on every output; the full workload sizes are
+compared on sampled rows (stream boundaries, window edges, first/last tokens,
+tile edges, random interior rows).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from latent_sequence_length_amd import hd, synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+INTRA, CROSS = 0, 1
+
+
+@pytest.fixture(autouse=True)
+def announce(request):
+    sys.__stdout__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+    sys.__stdout__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def to_np(t):
+    if isinstance(t, np.ndarray):
+        return t.astype(np.float64)
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def check_bf16(got, want, what, max_abs=2e-2, mean_abs=2e-3):
+    diff = np.abs(to_np(got).reshape(want.shape) - want)
+    assert np.isfinite(diff).all(), f"{what}: non-finite output"
+    assert diff.max() <= max_abs, f"{what}: max abs {diff.max():.3e} > {max_abs}"
+    assert diff.mean() <= mean_abs, f"{what}: mean abs {diff.mean():.3e} > {mean_abs}"
+
+
+def check_f32(got, want, what, tol=1e-4):
+    diff = np.abs(to_np(got).reshape(want.shape) - want)
+    assert np.isfinite(diff).all(), f"{what}: non-finite output"
+    assert diff.max() <= tol, f"{what}: max abs {diff.max():.3e} > {tol}"
+
+
+def bits(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.view(torch.int32).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Expansion
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,L,n,V,D,dtype", [
+    (1, 64, 2, 512, 64, torch.float32),     # tiny oracle case
+    (1, 64, 1, 512, 64, torch.float32),     # n = 1 control
+    (3, 5, 16, 37, 7, torch.bfloat16),      # 14-byte rows (2-byte path), HD_MAX_STREAMS tables
+    (2, 9, 3, 11, 3, torch.float32),        # 12-byte rows
+    (2, 33, 4, 1000, 520, torch.bfloat16),  # 1040-byte rows: vector path + tail
+])
+def test_expand_embed_small(B, L, n, V, D, dtype):
+    tabs = synth.tables(n, V, D, dtype, DEV)
+    ids = synth.token_ids(B, L, V, device=DEV, force_edges=True)
+    out = hd.expand_embed(ids, tabs)
+    want = oracle.expand_embed(ids.cpu().numpy(), [t.cpu() for t in tabs])
+    np.testing.assert_array_equal(bits(out), want.view(np.uint16 if dtype == torch.bfloat16 else np.int32))
+
+
+def test_expand_embed_full_tables():
+    """64 sequences x 1 new token x 4 streams, then 4096 tokens x 4 streams,
+    from four 160000 x 7168 bf16 tables: bit-exact against the oracle."""
+    c = synth.EMBED_DECODE
+    tabs = synth.tables(c["n"], c["V"], c["D"], c["dtype"], DEV)
+    host = [t.cpu() for t in tabs]
+    for B, L in ((c["B"], c["L"]), (synth.EMBED_PREFILL["B"], synth.EMBED_PREFILL["L"])):
+        ids = synth.token_ids(B, L, c["V"], device=DEV, force_edges=True)
+        out = hd.expand_embed(ids, tabs)
+        want = oracle.expand_embed(ids.cpu().numpy(), host)
+        np.testing.assert_array_equal(bits(out), want)
+
+
+# ---------------------------------------------------------------------------
+# Prefill
+# ---------------------------------------------------------------------------
+
+def run_fwd(shape_args, mode, window, dtype, scale=0.0):
+    B, L, n, Hq, Hkv, d = shape_args
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, dtype, DEV)
+    o, lse = hd.sfa_fwd(q, k, v, n, mode, window, scale, return_lse=True)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse
+
+
+@pytest.mark.parametrize("n", [1, 2])
+@pytest.mark.parametrize("mode", [INTRA, CROSS])
+def test_fwd_f32_tiny(n, mode):
+    shape = (1, 64, n, 4, 4, 32)
+    q, k, v, o, lse = run_fwd(shape, mode, 0, torch.float32)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), n, mode)
+    check_f32(o, want, "o")
+    check_f32(lse, wlse, "lse")
+
+
+@pytest.mark.parametrize("shape,mode,window", [
+    ((2, 37, 3, 4, 2, 64), INTRA, 5),
+    ((1, 50, 2, 2, 1, 128), CROSS, 7),
+    ((1, 19, 4, 8, 1, 32), INTRA, 0),
+])
+def test_fwd_f32_shapes(shape, mode, window):
+    q, k, v, o, lse = run_fwd(shape, mode, window, torch.float32)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), shape[2], mode, window)
+    check_f32(o, want, "o")
+    check_f32(lse, wlse, "lse")
+
+
+BF16_SHAPES = [
+    # (B, L, n, Hq, Hkv, d), mode, window
+    ((1, 64, 2, 4, 4, 32), INTRA, 0),
+    ((1, 64, 2, 4, 4, 32), CROSS, 0),
+    ((2, 200, 3, 8, 2, 128), INTRA, 0),     # g=4, ragged tail
+    ((2, 200, 3, 8, 2, 128), CROSS, 0),
+    ((1, 257, 4, 8, 8, 64), INTRA, 0),      # MHA: 4 token blocks per workgroup
+    ((1, 130, 4, 16, 2, 128), CROSS, 0),    # g=8: two head groups
+    ((1, 97, 2, 6, 3, 64), INTRA, 0),       # g=2
+    ((1, 300, 1, 8, 2, 128), INTRA, 0),     # n=1
+    ((1, 300, 4, 8, 2, 128), INTRA, 1),     # window of one token: o = v
+    ((1, 300, 4, 8, 2, 128), INTRA, 70),    # window edge inside tiles
+    ((1, 160, 4, 8, 2, 128), CROSS, 10),    # local cross-stream (mask b)
+    ((1, 160, 4, 8, 2, 32), CROSS, 33),
+    ((3, 1, 4, 4, 1, 128), INTRA, 0),       # one token
+    ((1, 1, 1, 2, 1, 64), CROSS, 0),        # one position
+    ((1, 129, 3, 4, 2, 128), CROSS, 1000),  # window wider than the sequence
+]
+
+
+@pytest.mark.parametrize("shape,mode,window", BF16_SHAPES)
+def test_fwd_bf16_vs_oracle(shape, mode, window):
+    q, k, v, o, lse = run_fwd(shape, mode, window, torch.bfloat16)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), shape[2], mode, window)
+    check_bf16(o, want, f"o {shape} mode={mode} W={window}")
+    check_f32(lse, wlse, "lse", tol=1e-3)
+
+
+def test_fwd_bf16_custom_scale():
+    shape = (1, 70, 2, 4, 2, 64)
+    q, k, v, o, lse = run_fwd(shape, CROSS, 0, torch.bfloat16, scale=0.05)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), 2, CROSS, 0, 0.05)
+    check_bf16(o, want, "o scale=0.05")
+    check_f32(lse, wlse, "lse", tol=1e-3)
+
+
+def sample_rows(B, L, n, Hq, window, count, seed):
+    """Flat query rows (b*nL + t)*Hq + h covering edges and random interior."""
+    rng = np.random.default_rng(seed)
+    toks = {0, 1, L - 1, L - 2, L // 2}
+    for e in (31, 32, 63, 64, 127, 128):
+        toks.update({e, L - 1 - e})
+    if window:
+        toks.update({window - 1, window, window + 1, L - window})
+    toks = [i for i in toks if 0 <= i < L]
+    rows = []
+    for i in toks:
+        for s in range(n):
+            for h in (0, Hq - 1, int(rng.integers(Hq))):
+                b = int(rng.integers(B))
+                rows.append((b * n * L + i * n + s) * Hq + h)
+    while len(rows) < count:
+        b, t, h = rng.integers(B), rng.integers(n * L), rng.integers(Hq)
+        rows.append(int((b * n * L + t) * Hq + h))
+    return np.unique(np.array(rows, dtype=np.int64))
+
+
+FULL = [synth.INTRA_4K, synth.INTRA_4K_N1, synth.CROSS_4K, synth.LONG_INTRA_W, synth.LONG_CROSS]
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
+def test_fwd_full_size_sampled(cfg):
+    count = 512 if cfg is synth.LONG_CROSS else 4096
+    q, k, v, o, lse = run_fwd((cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d), cfg.mode, cfg.window, cfg.dtype)
+    rows = sample_rows(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.window, count, seed=11)
+    want, wlse = oracle.sfa_rows(q.cpu(), k.cpu(), v.cpu(), cfg.n, cfg.mode, cfg.window, rows=rows)
+    got = o.reshape(-1, cfg.d)[torch.from_numpy(rows).to(DEV)]
+    check_bf16(got, want, cfg.name)
+    nL = cfg.n * cfg.L
+    b, t, h = rows // (nL * cfg.Hq), (rows // cfg.Hq) % nL, rows % cfg.Hq
+    check_f32(lse.cpu().numpy()[b, h, t], wlse, "lse", tol=1e-3)
+    assert torch.isfinite(o).all()
+
+
+def test_fwd_deterministic_and_guarded():
+    shape = (1, 300, 4, 8, 2, 128)
+    B, L, n, Hq, Hkv, d = shape
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.bfloat16, DEV)
+    for mode, window in ((INTRA, 0), (CROSS, 0), (INTRA, 50)):
+        guard = 4096
+        buf = torch.full((q.numel() + 2 * guard,), -7.0, dtype=torch.bfloat16, device=DEV)
+        o1 = buf[guard:guard + q.numel()].view(q.shape)
+        hd.hd_sfa_fwd(q, k, v, o1, n, mode, window)
+        o2 = hd.sfa_fwd(q, k, v, n, mode, window)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert (buf[:guard] == -7.0).all() and (buf[guard + q.numel():] == -7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+def run_decode(B, n, Hq, Hkv, d, T_cap, lens, mode, window, dtype):
+    q, kn, vn, kc, vc = synth.decode_inputs(B, n, Hq, Hkv, d, T_cap, dtype, DEV)
+    kc0, vc0 = kc.cpu(), vc.cpu()
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = hd.sfa_decode(q, kn, vn, kc, vc, cl, mode, window)
+    torch.cuda.synchronize()
+    return q, kn, vn, kc0, vc0, kc, vc, o
+
+
+DEC_SHAPES = [
+    # B, n, Hq, Hkv, d, T_cap, lens
+    (3, 4, 8, 2, 128, 40, [0, 5, 37]),      # 16 query rows per kv head
+    (2, 2, 4, 4, 32, 70, [69, 1]),          # g=1
+    (2, 4, 16, 2, 64, 33, [32, 7]),         # 32 rows: two query blocks
+    (1, 8, 32, 4, 128, 20, [19]),           # 64 rows: four query blocks
+    (2, 3, 10, 2, 128, 50, [11, 48]),       # 15 rows: padded block
+    (2, 1, 8, 1, 128, 300, [299, 150]),     # n=1
+]
+
+
+@pytest.mark.parametrize("shape", DEC_SHAPES)
+@pytest.mark.parametrize("mode,window", [(INTRA, 0), (CROSS, 0), (INTRA, 3), (CROSS, 2)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_decode_vs_oracle(shape, mode, window, dtype):
+    B, n, Hq, Hkv, d, T_cap, lens = shape
+    q, kn, vn, kc0, vc0, kc, vc, o = run_decode(B, n, Hq, Hkv, d, T_cap, lens, mode, window, dtype)
+    want = oracle.sfa_decode(q.cpu(), kn.cpu(), vn.cpu(), kc0, vc0, lens, mode, window)
+    if dtype == torch.bfloat16:
+        check_bf16(o, want, f"decode {shape} mode={mode} W={window}")
+    else:
+        check_f32(o, want, f"decode {shape} mode={mode} W={window}")
+    np.testing.assert_array_equal(bits(kc), oracle.decode_append(kn.cpu(), kc0, lens).view(bits(kc).dtype))
+    np.testing.assert_array_equal(bits(vc), oracle.decode_append(vn.cpu(), vc0, lens).view(bits(vc).dtype))
+
+
+@pytest.mark.parametrize("mode", [INTRA, CROSS])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_decode_full_size_sampled(mode, ragged):
+    cfg = synth.DECODE_8K
+    T_cap = cfg.ctx + 8
+    if ragged:
+        lens = [int(x) for x in np.random.default_rng(5).integers(0, T_cap, cfg.B)]
+        lens[0], lens[-1] = 0, T_cap - 1
+    else:
+        lens = [cfg.ctx] * cfg.B
+    q, kn, vn, kc, vc = synth.decode_inputs(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, T_cap, cfg.dtype, DEV)
+    picks = [0, 17, 42, cfg.B - 1]
+    kc0 = [kc[b].cpu() for b in picks]
+    vc0 = [vc[b].cpu() for b in picks]
+    cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o = hd.sfa_decode(q, kn, vn, kc, vc, cl, mode, 0)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all()
+    for j, b in enumerate(picks):
+        want = oracle.sfa_decode(q[b:b + 1].cpu(), kn[b:b + 1].cpu(), vn[b:b + 1].cpu(), kc0[j][None],
+                                 vc0[j][None], [lens[b]], mode, 0)
+        check_bf16(o[b:b + 1], want, f"decode b={b} len={lens[b]} mode={mode}")
+        got_row = bits(kc[b, lens[b]])
+        np.testing.assert_array_equal(got_row, bits(kn[b]))
+
+
+def test_decode_deterministic_and_guarded():
+    B, n, Hq, Hkv, d, T_cap = 4, 4, 32, 8, 128, 600
+    q, kn, vn, kc, vc = synth.decode_inputs(B, n, Hq, Hkv, d, T_cap, torch.bfloat16, DEV)
+    cl = torch.tensor([599, 0, 300, 64], dtype=torch.int32, device=DEV)
+    for mode in (INTRA, CROSS):
+        guard = 2048
+        buf = torch.full((q.numel() + 2 * guard,), 3.0, dtype=torch.bfloat16, device=DEV)
+        o1 = buf[guard:guard + q.numel()].view(q.shape)
+        ws = torch.full((hd.hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap) + 4096,), 255,
+                        dtype=torch.uint8, device=DEV)
+        hd.hd_sfa_decode(q, kn, vn, kc, vc, cl, o1, mode, 0, 0.0, ws)
+        o2 = hd.sfa_decode(q, kn, vn, kc, vc, cl, mode)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2)
+        assert (buf[:guard] == 3.0).all() and (buf[guard + q.numel():] == 3.0).all()
