@@ -211,6 +211,258 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Head dim 128 fast path.  Same math and work decomposition as above, plus:
+//   * K and V tiles are fetched with direct-to-LDS 16-byte loads
+//     (global_load_lds), double-buffered: tile t+1 is in flight while tile t
+//     is computed, with no VGRPs spent on staging and one barrier per tile;
+//   * LDS rows are 256 B with the 16-byte chunk index XOR-swizzled by the row
+//     (sw(r) = 2*(r%8) + (r/8)%2), so the K-operand reads (16 rows, one chunk)
+//     and the transposed V reads (8 rows, four chunks) are bank-conflict free;
+//   * the V^T operand comes from two ds_read_b64_tr_b16 per MFMA: within each
+//     16-lane group that instruction returns out[i][e] = in[4e + i/4][i%4],
+//     so lane j of the group addresses key row r0 + j/4, dims d0 + 4*(j%4);
+//   * softmax: the scale is folded into one fma before exp2, the running max
+//     is only raised when a tile's max exceeds it by more than 8 (log2 units),
+//     so the O rescale is skipped on almost every tile (p <= 2^8 keeps fp32
+//     sums and bf16 P exact enough; the final normalisation is unchanged);
+//   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
+//     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Direct-to-LDS 16-byte load: lane l's 16 bytes from gptr land at LDS byte
+// address lds_base + 16*l.  Issued as a two-instruction asm block (M0 holds
+// the wave-uniform LDS base) so that the compiler's wait-count pass does not
+// treat the in-flight copy into one buffer as aliasing the transposed reads of
+// the other buffer; the kernel waits for it explicitly (vmcnt(0) + barrier)
+// before the tile is read.  No other code in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const void *gptr, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const char *p) {
+    return (unsigned)(size_t)((__attribute__((address_space(3))) const char *)p);
+}
+
+__device__ __forceinline__ int swz128(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// One tile of the d=128 loop: wait for tile `it` (in buffer `cur`), start
+// the DMA of tile it+1 into `nxt`, then compute tile `it`.  `cur` and `nxt`
+// are distinct __shared__ arrays known at compile time, so the compiler can
+// tell the in-flight DMA and this tile's LDS reads apart.
+struct D128State {
+    f32x16 oacc[4];
+    float m_run, l_run;
+};
+
+template <typename Issue>
+__device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&issue_next, bool has_next,
+                                          int t0, const FwdArgs &p, int qw0, int myq, int hi, int l32, int l16,
+                                          int g2, const bf16x8 (&qop)[8], float scale_log2, D128State &st) {
+    constexpr int D = 128;
+    constexpr int TILE = KT * D * 2;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
+    __syncthreads();                // ... and every wave's; the previous tile is fully consumed
+    if (has_next) issue_next();
+
+    const bool active = (t0 <= qw0 + QW - 1) && (p.weff == 0 || t0 + KT - 1 > qw0 - p.weff);
+    if (!active) return;
+    const bool need_mask = (t0 + KT - 1 > qw0) || (t0 + KT > p.Lsub) ||
+                           (p.weff != 0 && t0 <= qw0 + QW - 1 - p.weff);
+    const char *kbuf = cur;
+    const char *vbuf = cur + TILE;
+
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        sacc[kb] = f32x16{};
+        const int r = kb * 32 + l32;
+        const char *row = kbuf + r * 256;
+        const int sw = swz128(r);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(row + (((2 * ks + hi) ^ sw) << 4));
+            sacc[kb] = mfma32(a, qop[ks], sacc[kb]);
+        }
+    }
+
+    float mx = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const bool vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+            }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+    mx = pair_max(mx);
+    const float m_tile = mx * scale_log2;
+    const float m_new = (m_tile > st.m_run + 8.f) ? m_tile : st.m_run;
+    const float alpha = (m_new == st.m_run) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
+    }
+    st.l_run *= alpha;
+    st.m_run = m_new;
+    const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int m2 = 0; m2 < 2; ++m2) {
+            bf16x8 pop;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
+                lsum += pv;
+                pop[j] = (bf16)pv;
+            }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                s16x4 half[2];
+#pragma unroll
+                for (int jh = 0; jh < 2; ++jh) {
+                    const int row = kb * 32 + 16 * m2 + 8 * jh + 4 * hi + (l16 >> 2);
+                    const int dim = db * 32 + 16 * g2 + 4 * (l16 & 3);
+                    const char *addr = vbuf + row * 256 + (((dim >> 3) ^ swz128(row)) << 4) + ((dim >> 2) & 1) * 8;
+                    half[jh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(addr));
+                }
+                const s16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                st.oacc[db] = mfma32(__builtin_bit_cast(bf16x8, both), pop, st.oacc[db]);
+            }
+        }
+    st.l_run += lsum;
+}
+
+__global__ __launch_bounds__(256, 2) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
+                                                                  float scale_log2) {
+    constexpr int D = 128;
+    constexpr int TILE = KT * D * 2;  // 16 KB per K or V tile
+    __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K | V, even tiles
+    __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];  // K | V, odd tiles
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int g = p.Hq / p.Hkv, ngrp = g / HG;
+
+    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
+    const int nwg = nrest * nqblk;
+    const int bid = blockIdx.x;
+    const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    const int qblk = nqblk - 1 - lid % nqblk;
+    int rest = lid / nqblk;
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int hgrp = rest % ngrp; rest /= ngrp;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+
+    const int QB = QW * TB;
+    const int q0 = qblk * QB;
+    const int hw = wave % HG, tb = wave / HG;
+    const int h = kvh * g + hgrp * HG + hw;
+    const int qw0 = q0 + tb * QW;
+    const int myq = qw0 + l32;
+    const bool qvalid = myq < p.Lsub;
+
+    const int64_t qrs = (int64_t)p.Hq * D;
+    const int64_t krs = (int64_t)p.Hkv * D;
+    const int64_t bpos = (int64_t)b * p.nL + sub;
+    const bf16 *qg = static_cast<const bf16 *>(p.q);
+    const bf16 *kg = static_cast<const bf16 *>(p.k) + (int64_t)kvh * D;
+    const bf16 *vg = static_cast<const bf16 *>(p.v) + (int64_t)kvh * D;
+
+    const int kend = min(q0 + QB, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    const int tfirst = kbeg & ~(KT - 1);
+    const int ntiles = (kend - tfirst + KT - 1) / KT;
+
+    // Each wave moves 4 x 1 KB of K and of V per tile: slots w*256 .. +255,
+    // slot s = row*16 + physical chunk; lane l of instruction i fills slot
+    // (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).
+    auto issue = [&](int t0, char *dst) {
+        char *kb = dst;
+        char *vb = dst + TILE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s0 = (wave * 4 + i) * 64;
+            const int s = s0 + lane;
+            const int r = s >> 4;
+            const int c = (s & 15) ^ swz128(r);
+            const int j = min(t0 + r, p.Lsub - 1);
+            const int64_t off = (bpos + (int64_t)j * p.stride) * krs + c * 8;
+            lds_dma16(kg + off, lds_addr(kb + s0 * 16));
+            lds_dma16(vg + off, lds_addr(vb + s0 * 16));
+        }
+    };
+    if (ntiles > 0) issue(tfirst, buf0);
+
+    bf16x8 qop[D / 16];
+    {
+        const bf16 *qp = qg + (bpos + (int64_t)(qvalid ? myq : 0) * p.stride) * qrs + (int64_t)h * D;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
+            qop[ks] = qvalid ? x : bf16x8{};
+        }
+    }
+
+    D128State st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.oacc[db] = f32x16{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    for (int it = 0; it < ntiles; it += 2) {
+        const int t0 = tfirst + it * KT;
+        d128_tile(buf0, [&] { issue(t0 + KT, buf1); }, it + 1 < ntiles, t0, p, qw0, myq, hi, l32, l16, g2, qop,
+                  scale_log2, st);
+        if (it + 1 < ntiles)
+            d128_tile(buf1, [&] { issue(t0 + 2 * KT, buf0); }, it + 2 < ntiles, t0 + KT, p, qw0, myq, hi, l32,
+                      l16, g2, qop, scale_log2, st);
+    }
+
+    const float l_tot = pair_sum(st.l_run);
+    if (qvalid) {
+        const float inv = 1.f / l_tot;
+        const int64_t pos = bpos + (int64_t)myq * p.stride;
+        bf16 *op = static_cast<bf16 *>(p.o) + pos * qrs + (int64_t)h * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                bf16x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = (bf16)(st.oacc[db][4 * r4 + e] * inv);
+                *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * r4 + 4 * hi) = y;
+            }
+        if (p.lse != nullptr && hi == 0)
+            p.lse[((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL)] = st.m_run * kLn2 + __logf(l_tot);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
@@ -229,7 +481,8 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
             hipLaunchKernelGGL(sfa_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
             break;
         case 128:
-            hipLaunchKernelGGL(sfa_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
+            hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk,
+                               sl2);
             break;
         default:
             return hipErrorInvalidValue;
