@@ -1,0 +1,52 @@
+// attn_common.h -- device helpers shared by the bf16 attention kernels
+// (internal to libhd.so).
+#pragma once
+
+#include "hd_internal.h"
+
+namespace hd {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Direct-to-LDS 16-byte load: lane l's 16 bytes from gptr land at LDS byte
+// address lds_base + 16*l.  Issued as a two-instruction asm block (M0 holds
+// the wave-uniform LDS base) so that the compiler's wait-count pass does not
+// treat the in-flight copy into one buffer as aliasing the transposed reads of
+// the other buffer; the kernel waits for it explicitly (vmcnt(0) + barrier)
+// before the tile is read.  No other code in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const void *gptr, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const char *p) {
+    return (unsigned)(size_t)((__attribute__((address_space(3))) const char *)p);
+}
+
+constexpr bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
+
+__device__ __forceinline__ int swz128(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+__device__ __forceinline__ float pair_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+
+// One ds_read_b64_tr_b16 from an LDS address.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char *addr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(addr));
+}
+
+}  // namespace hd

@@ -23,7 +23,7 @@
 //
 // 16x16x32 bf16 operand layout: lane l supplies row (l % 16) of A / column of
 // B and k-slots 8*(l/16) .. +7; the accumulator holds C[4*(l/16) + i][l % 16].
-#include "hd_internal.h"
+#include "attn_common.h"
 
 namespace hd {
 
@@ -40,6 +40,22 @@ struct Split {
     int chunk;   // tokens per split
     int nsplit;  // splits per (b, kv head)
 };
+
+bool use_d128_path(int n, int d) { return d == 128 && 64 % n == 0; }
+
+Split choose_split_d128(int B, int Hkv, int T_cap) {
+    // One workgroup per CU (128 KB LDS): aim for ~4096 workgroups, chunks of
+    // >= 64 tokens in multiples of 16.
+    const int64_t bh = (int64_t)B * Hkv;
+    const int64_t want = (4096 + bh - 1) / bh;
+    int64_t chunk = ((int64_t)T_cap + want - 1) / want;
+    chunk = ((chunk + 15) / 16) * 16;
+    if (chunk < 64) chunk = 64;
+    Split s;
+    s.chunk = (int)chunk;
+    s.nsplit = (int)(((int64_t)T_cap + chunk - 1) / chunk);
+    return s;
+}
 
 Split choose_split(int B, int Hkv, int T_cap) {
     // Aim for at least ~2048 workgroups (8 per CU) so enough cache bytes are in
@@ -271,6 +287,262 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
     }
 }
 
+// ---------------------------------------------------------------------------
+// Head dim 128, n dividing 64: bandwidth-oriented partial kernel.
+//   * the workgroup streams its chunk in tiles of 64 cache rows (64/n tokens x
+//     n streams) of K and V, 32 KB per tile, copied straight into LDS with
+//     direct-to-LDS loads and kept three tiles ahead (4 buffers, 96 KB in
+//     flight per CU): the copy engine, not the waves, carries the bytes;
+//   * rows of token len come from k_new / v_new (selected per lane, no
+//     branches); rows past the chunk re-read its last row and are masked;
+//   * wave w scores rows 16w .. 16w+15 of every tile against all n*g query
+//     rows (16-row blocks): S^T with v_mfma_f32_16x16x32_bf16, whose
+//     accumulator layout is exactly the B operand of v_mfma_f32_16x16x16_bf16
+//     for PV (lane l: query l%16, keys 4*(l/16) .. +3), and the V^T operand is
+//     one ds_read_b64_tr_b16 (a 16-lane group reads 4 rows x 16 dims).
+//   LDS rows are 256 B with the chunk swizzle sw(r) used by the prefill.
+constexpr int DT_ROWS = 64;                    // cache rows per tile
+constexpr int DT_TILE = DT_ROWS * 128 * 2;     // bytes of one K (or V) tile
+constexpr int DT_NBUF = 4;
+
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16(bf16x4v a, bf16x4v b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+template <int NQB>
+__global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, Split sp, float scale_log2) {
+    constexpr int D = 128;
+    constexpr int TILES_BYTES = DT_NBUF * 2 * DT_TILE;
+    constexpr int MERGE_BYTES = NW * NQB * 16 * (2 + D) * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[TILES_BYTES > MERGE_BYTES ? TILES_BYTES : MERGE_BYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, grp = lane >> 4;
+    const int split = blockIdx.x, bh = blockIdx.y;
+    const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
+    const int n = p.n, g = p.Hq / p.Hkv, QR = n * g;
+    const int len = p.cache_len[b];
+    const int c0 = split * sp.chunk;
+    if (c0 > len) return;  // nothing cached here yet; the combine skips it
+    const int c1 = min(c0 + sp.chunk, len + 1);
+
+    const bf16 *kn = static_cast<const bf16 *>(p.k_new);
+    const bf16 *vn = static_cast<const bf16 *>(p.v_new);
+    bf16 *kc = static_cast<bf16 *>(p.k_cache);
+    bf16 *vc = static_cast<bf16 *>(p.v_cache);
+    const int64_t hstride = (int64_t)p.Hkv * D;       // elements between streams of one token
+    const int64_t cache_tok = (int64_t)n * hstride;   // elements per cached token
+    const int64_t cache_b = (int64_t)b * p.T_cap * cache_tok + (int64_t)kvh * D;
+    const int64_t new_b = (int64_t)b * n * hstride + (int64_t)kvh * D;
+
+    // Append the new token's rows of this kv head (row len is read by nobody).
+    if (len < c1) {
+        for (int c = tid; c < n * (D / 8); c += 256) {
+            const int s = c / (D / 8), cc = c - s * (D / 8);
+            const int64_t src = new_b + (int64_t)s * hstride + cc * 8;
+            const int64_t dst = cache_b + (int64_t)len * cache_tok + (int64_t)s * hstride + cc * 8;
+            *reinterpret_cast<uint4 *>(kc + dst) = *reinterpret_cast<const uint4 *>(kn + src);
+            *reinterpret_cast<uint4 *>(vc + dst) = *reinterpret_cast<const uint4 *>(vn + src);
+        }
+    }
+
+    // Rows (flat token*n + stream) of this chunk inside the window.
+    const int tlo = p.window ? max(c0, len - p.window) : c0;
+    const int row_lo = tlo * n, row_hi = c1 * n;
+    const int ntiles = row_hi > row_lo ? (row_hi - row_lo + DT_ROWS - 1) / DT_ROWS : 0;
+
+    // Copy-in mapping: wave w, instruction i covers slots (4w+i)*64 .. +63 of
+    // the tile (slot = row*16 + physical chunk); n divides 64, so the row's
+    // token offset and stream are fixed per lane.
+    int ltok[4], lstream[4], lchunk[4], lrow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = (wave * 4 + i) * 4 + (lane >> 4);
+        lrow[i] = r;
+        ltok[i] = r / n;
+        lstream[i] = r - ltok[i] * n;
+        lchunk[i] = ((lane & 15) ^ swz128(r)) * 8;
+    }
+    const int tok_per_tile = DT_ROWS / n;
+    auto issue = [&](int t) {
+        char *dst = smem + (t % DT_NBUF) * 2 * DT_TILE;
+        const int tok0 = tlo + t * tok_per_tile;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int tok = tok0 + ltok[i];
+            const int last = (row_hi - 1) / n;  // rows past the chunk re-read its last token
+            const bool past = (tok - tlo) * n + lstream[i] >= row_hi - row_lo;
+            tok = past ? last : tok;
+            const int s = past ? (row_hi - 1) - last * n : lstream[i];
+            const int64_t coff = cache_b + (int64_t)tok * cache_tok + (int64_t)s * hstride + lchunk[i];
+            const int64_t noff = new_b + (int64_t)s * hstride + lchunk[i];
+            const bool is_new = tok >= len;
+            const bf16 *ksrc = is_new ? kn + noff : kc + coff;
+            const bf16 *vsrc = is_new ? vn + noff : vc + coff;
+            const int s0 = (wave * 4 + i) * 64;
+            lds_dma16(ksrc, lds_addr(dst + s0 * 16));
+            lds_dma16(vsrc, lds_addr(dst + DT_TILE + s0 * 16));
+        }
+    };
+    // Query operands: block qb, lane column l16 is query row c = qb*16 + l16
+    // (row c <-> stream c / g, head kvh*g + c % g); slots grp hold dims
+    // ks*32 + 8*grp .. +7.
+    const bf16 *qg = static_cast<const bf16 *>(p.q);
+    bf16x8 qop[NQB][D / 32];
+    int qstream[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        const int c = qb * 16 + l16;
+        const bool ok = c < QR;
+        const int s = ok ? c / g : 0, hh = ok ? c - s * g : 0;
+        qstream[qb] = s;
+        const bf16 *qp = qg + (((int64_t)b * n + s) * p.Hq + kvh * g + hh) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 32);
+            qop[qb][ks] = ok ? x : bf16x8{};
+        }
+    }
+
+    // The append stores and query loads complete before any copy is issued,
+    // so the explicit vmcnt waits below count only this wave's tile copies.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int t = 0; t < DT_NBUF - 1 && t < ntiles; ++t) issue(t);
+
+    f32x4 oacc[NQB][D / 16];
+    float m_run[NQB], l_run[NQB];
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) oacc[qb][db] = f32x4{};
+    }
+
+    // This lane's K operand row (16w + l16) and transposed-V row (16w + 4*grp + l16/4).
+    const int krow = 16 * wave + l16;
+    const int kx = swz128(krow);
+    const int vrow = 16 * wave + 4 * grp + (l16 >> 2);
+    const int vsw = swz128(vrow);
+    const int vhalf = (l16 & 1) * 8;
+    const int vc_lo = (l16 & 3) >> 1;
+    const int64_t tq_base = (int64_t)len * n;
+
+    for (int t = 0; t < ntiles; ++t) {
+        // Tile t has landed; the (up to two) newer tiles already issued, 8
+        // copies each, may stay in flight.  gfx9 s_waitcnt immediates:
+        // 0x4F70 = vmcnt(16), 0x0F78 = vmcnt(8).
+        const int newer = min(ntiles - 1 - t, DT_NBUF - 2);
+        if (newer >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);
+        else if (newer == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
+        else __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // ... for every wave; tile t-1 fully consumed
+        if (t + DT_NBUF - 1 < ntiles) issue(t + DT_NBUF - 1);
+        const char *kbuf = smem + (t % DT_NBUF) * 2 * DT_TILE;
+        const char *vbuf = kbuf + DT_TILE;
+
+        bf16x8 kop[D / 32];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            kop[ks] = *reinterpret_cast<const bf16x8 *>(kbuf + krow * 256 + (((4 * ks + grp) ^ kx) << 4));
+        bf16x4v vop[D / 16];
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const s16x4 x = lds_read_tr16(vbuf + vrow * 256 + (((2 * db + vc_lo) ^ vsw) << 4) + vhalf);
+            vop[db] = __builtin_bit_cast(bf16x4v, x);
+        }
+
+        const int rtile = row_lo + t * DT_ROWS + 16 * wave + 4 * grp;  // this lane's first key row
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            f32x4 sacc = {};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) sacc = mfma16(kop[ks], qop[qb][ks], sacc);
+            const int sq = qstream[qb];
+            const int64_t tq = tq_base + sq;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = rtile + i;
+                const int tok = r / n;
+                const int sk = r - tok * n;
+                bool vis = r < row_hi;
+                if (p.mode == 0) vis = vis && sk == sq && (p.window == 0 || len - tok < p.window);
+                else vis = vis && r <= tq && (p.window == 0 || tq - r < (int64_t)n * p.window);
+                sacc[i] = vis ? sacc[i] : -INFINITY;
+                mx = fmaxf(mx, sacc[i]);
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_tile = mx * scale_log2;
+            const float m_new = (m_tile > m_run[qb] + 8.f) ? m_tile : m_run[qb];
+            const float alpha = (m_new == m_run[qb]) ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+            const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+            bf16x4v pop;
+            float lsum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[i], scale_log2, neg_m));
+                lsum += pv;
+                pop[i] = (bf16)pv;
+            }
+            if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                for (int db = 0; db < D / 16; ++db) oacc[qb][db] *= alpha;
+            }
+            l_run[qb] = l_run[qb] * alpha + lsum;
+            m_run[qb] = m_new;
+#pragma unroll
+            for (int db = 0; db < D / 16; ++db) oacc[qb][db] = mfma16x16(vop[db], pop, oacc[qb][db]);
+        }
+    }
+    __syncthreads();  // tile buffers are reused for the merge below
+
+    float *ml = reinterpret_cast<float *>(smem);  // [4][NQB*16][2]
+    float *ow = ml + NW * NQB * 16 * 2;           // [4][NQB*16][D]
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb) {
+        float lt = l_run[qb];
+        lt += __shfl_xor(lt, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        const int c = qb * 16 + l16;
+        if (grp == 0) {
+            ml[(wave * NQB * 16 + c) * 2 + 0] = m_run[qb];
+            ml[(wave * NQB * 16 + c) * 2 + 1] = lt;
+        }
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ow[(wave * NQB * 16 + c) * D + db * 16 + 4 * grp + i] = oacc[qb][db][i];
+    }
+    __syncthreads();
+    const int64_t part = ((int64_t)bh * sp.nsplit + split) * QR;
+    float *ws_acc = p.ws;
+    float *ws_ml = p.ws + (int64_t)p.B * p.Hkv * sp.nsplit * QR * D;
+    for (int e = tid; e < QR * D; e += 256) {
+        const int c = e / D, dim = e - c * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, ml[(w * NQB * 16 + c) * 2]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float acc = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(ml[(w * NQB * 16 + c) * 2] - Mu);
+            acc += wt * ow[(w * NQB * 16 + c) * D + dim];
+            L += wt * ml[(w * NQB * 16 + c) * 2 + 1];
+        }
+        ws_acc[(part + c) * D + dim] = acc;
+        if (dim == 0) {
+            ws_ml[(part + c) * 2 + 0] = M;
+            ws_ml[(part + c) * 2 + 1] = L;
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp) {
     const int lane = threadIdx.x & 63;
@@ -351,13 +623,37 @@ hipError_t launch_d(const DecArgs &a, Split sp, float sl2, hipStream_t st) {
 }  // namespace
 
 size_t decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap) {
-    const Split sp = choose_split(B, Hkv, T_cap);
+    const Split sp = use_d128_path(n, d) ? choose_split_d128(B, Hkv, T_cap) : choose_split(B, Hkv, T_cap);
     return (size_t)B * n * Hq * sp.nsplit * (size_t)(d + 2) * sizeof(float);
 }
 
+template <int NQB>
+hipError_t launch_partial_d128(const DecArgs &a, Split sp, float sl2, hipStream_t st) {
+    hipLaunchKernelGGL((decode_partial_d128_kernel<NQB>), dim3(sp.nsplit, a.B * a.Hkv), dim3(256), 0, st, a, sp,
+                       sl2);
+    return hipGetLastError();
+}
+
 hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st) {
-    const Split sp = choose_split(a.B, a.Hkv, a.T_cap);
     const float sl2 = a.scale * kLog2e;
+    if (use_d128_path(a.n, a.d)) {
+        const Split sp = choose_split_d128(a.B, a.Hkv, a.T_cap);
+        const int QR = a.n * (a.Hq / a.Hkv);
+        hipError_t e;
+        switch ((QR + 15) / 16) {
+            case 1: e = launch_partial_d128<1>(a, sp, sl2, st); break;
+            case 2: e = launch_partial_d128<2>(a, sp, sl2, st); break;
+            case 3: e = launch_partial_d128<3>(a, sp, sl2, st); break;
+            case 4: e = launch_partial_d128<4>(a, sp, sl2, st); break;
+            default: return hipErrorInvalidValue;
+        }
+        if (e != hipSuccess) return e;
+        const int64_t rows = (int64_t)a.B * a.Hkv * QR;
+        hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)((rows + NW - 1) / NW)), dim3(256), 0, st, a,
+                           sp);
+        return hipGetLastError();
+    }
+    const Split sp = choose_split(a.B, a.Hkv, a.T_cap);
     switch (a.d) {
         case 32: return launch_d<32>(a, sp, sl2, st);
         case 64: return launch_d<64>(a, sp, sl2, st);

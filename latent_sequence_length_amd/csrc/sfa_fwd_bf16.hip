@@ -27,7 +27,7 @@
 // (l / 32); A and B pair k-slots identically, so any consistent assignment of
 // real k indices to slots is a valid contraction.  The accumulator holds
 // C[8*(r/4) + 4*(l/32) + (r%4)][l % 32] in register r.
-#include "hd_internal.h"
+#include "attn_common.h"
 
 namespace hd {
 
@@ -36,10 +36,6 @@ namespace {
 constexpr int KT = 64;   // keys per tile
 constexpr int QW = 32;   // queries per wave
 constexpr int NWAVE = 4;
-
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ float wave_xor32(float x) {
     return __shfl_xor(x, 32, 64);
@@ -232,33 +228,6 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-// Direct-to-LDS 16-byte load: lane l's 16 bytes from gptr land at LDS byte
-// address lds_base + 16*l.  Issued as a two-instruction asm block (M0 holds
-// the wave-uniform LDS base) so that the compiler's wait-count pass does not
-// treat the in-flight copy into one buffer as aliasing the transposed reads of
-// the other buffer; the kernel waits for it explicitly (vmcnt(0) + barrier)
-// before the tile is read.  No other code in these kernels uses M0.
-__device__ __forceinline__ void lds_dma16(const void *gptr, unsigned lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gptr)
-                 : "memory", "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const char *p) {
-    return (unsigned)(size_t)((__attribute__((address_space(3))) const char *)p);
-}
-
-__device__ __forceinline__ int swz128(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ float pair_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // One tile of the d=128 loop: wait for tile `it` (in buffer `cur`), start
 // the DMA of tile it+1 into `nxt`, then compute tile `it`.  `cur` and `nxt`
 // are distinct __shared__ arrays known at compile time, so the compiler can
@@ -301,13 +270,17 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
 
     float mx = -INFINITY;
     if (need_mask) {
+        // visible <=> lo <= key <= hi, checked as one unsigned compare
+        const int lo = p.weff ? myq - p.weff + 1 : 0;
+        const int hi_key = min(myq, p.Lsub - 1);
+        const unsigned span = (unsigned)(hi_key - lo);
+        const int base = t0 + 4 * hi - lo;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                const bool vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
-                sacc[kb][r] = vis ? sacc[kb][r] : -INFINITY;
+                const unsigned u = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+                sacc[kb][r] = (u <= span) ? sacc[kb][r] : -INFINITY;
             }
     }
 #pragma unroll
@@ -333,11 +306,13 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
         for (int m2 = 0; m2 < 2; ++m2) {
             bf16x8 pop;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
-                lsum += pv;
-                pop[j] = (bf16)pv;
-            }
+            for (int j = 0; j < 8; ++j)
+                pop[j] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
+            // row sum of the bf16 probabilities that enter PV, two per dot2
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 0, 1), kOnes2, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 2, 3), kOnes2, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 4, 5), kOnes2, lsum, false);
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 6, 7), kOnes2, lsum, false);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 s16x4 half[2];
@@ -401,20 +376,25 @@ __global__ __launch_bounds__(256, 2) void sfa_fwd_bf16_d128_kernel(FwdArgs p, in
 
     // Each wave moves 4 x 1 KB of K and of V per tile: slots w*256 .. +255,
     // slot s = row*16 + physical chunk; lane l of instruction i fills slot
-    // (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).
+    // (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).  Rows past the end
+    // of the sub-sequence re-read its last row (finite data, masked later).
+    const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
+    int lrow[4], lchunk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lrow[i] = (wave * 4 + i) * 4 + (lane >> 4);
+        lchunk[i] = ((lane & 15) ^ swz128(lrow[i])) * 8;
+    }
     auto issue = [&](int t0, char *dst) {
-        char *kb = dst;
-        char *vb = dst + TILE;
+        const int64_t tbase = (bpos + (int64_t)t0 * p.stride) * krs;
+        const bf16 *kt = kg + tbase, *vt = vg + tbase;
+        const int rmax = p.Lsub - 1 - t0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const int off = min(lrow[i], rmax) * rstride + lchunk[i];
             const int s0 = (wave * 4 + i) * 64;
-            const int s = s0 + lane;
-            const int r = s >> 4;
-            const int c = (s & 15) ^ swz128(r);
-            const int j = min(t0 + r, p.Lsub - 1);
-            const int64_t off = (bpos + (int64_t)j * p.stride) * krs + c * 8;
-            lds_dma16(kg + off, lds_addr(kb + s0 * 16));
-            lds_dma16(vg + off, lds_addr(vb + s0 * 16));
+            lds_dma16(kt + off, lds_addr(dst + s0 * 16));
+            lds_dma16(vt + off, lds_addr(dst + TILE + s0 * 16));
         }
     };
     if (ntiles > 0) issue(tfirst, buf0);
@@ -481,6 +461,11 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
             hipLaunchKernelGGL(sfa_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
             break;
         case 128:
+            if ((int64_t)KT * a.stride * a.Hkv * 128 >= (int64_t)1 << 31) {  // 32-bit lane offsets
+                hipLaunchKernelGGL(sfa_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk,
+                                   sl2);
+                break;
+            }
             hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk,
                                sl2);
             break;
