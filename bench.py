@@ -215,14 +215,14 @@ def main():
         ach = fl / report["intra_n4"]["ms"] / 1e9
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "sfa_fwd_bf16_kernel<128>", "per_launch_flops": fl}
+                "kernel": "sfa_fwd_bf16_d128_kernel", "per_launch_flops": fl}
     roof_dec = None
     if "decode_intra" in report:
         by = comps["decode_intra"][2]
         ach = by / report["decode_intra"]["ms"] / 1e6
         roof_dec = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBPS, 4), "per_launch_bytes": by,
-                    "kernels": "decode_partial_kernel<128,1> + decode_combine_kernel<128>"}
+                    "kernels": "decode_partial_d128_kernel<1> + decode_combine_kernel<128>"}
 
     line = {
         "metric": "stream-factorized attn TFLOP/s (useful) at n=4 + n4/n1 time ratio; decode GB/s",

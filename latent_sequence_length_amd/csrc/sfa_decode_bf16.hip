@@ -25,6 +25,13 @@
 // B and k-slots 8*(l/16) .. +7; the accumulator holds C[4*(l/16) + i][l % 16].
 #include "attn_common.h"
 
+#ifndef HD_DECODE_NBUF
+#define HD_DECODE_NBUF 4      // tile buffers (copies run NBUF-1 tiles ahead)
+#endif
+#ifndef HD_DECODE_TARGET_WGS
+#define HD_DECODE_TARGET_WGS 1024  // workgroups the d=128 split aims for
+#endif
+
 namespace hd {
 
 namespace {
@@ -44,10 +51,10 @@ struct Split {
 bool use_d128_path(int n, int d) { return d == 128 && 64 % n == 0; }
 
 Split choose_split_d128(int B, int Hkv, int T_cap) {
-    // One workgroup per CU (128 KB LDS): aim for ~4096 workgroups, chunks of
-    // >= 64 tokens in multiples of 16.
+    // One workgroup per CU (128 KB LDS): aim for ~HD_DECODE_TARGET_WGS
+    // workgroups, chunks of >= 64 tokens in multiples of 16.
     const int64_t bh = (int64_t)B * Hkv;
-    const int64_t want = (4096 + bh - 1) / bh;
+    const int64_t want = (HD_DECODE_TARGET_WGS + bh - 1) / bh;
     int64_t chunk = ((int64_t)T_cap + want - 1) / want;
     chunk = ((chunk + 15) / 16) * 16;
     if (chunk < 64) chunk = 64;
@@ -303,7 +310,8 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
 //   LDS rows are 256 B with the chunk swizzle sw(r) used by the prefill.
 constexpr int DT_ROWS = 64;                    // cache rows per tile
 constexpr int DT_TILE = DT_ROWS * 128 * 2;     // bytes of one K (or V) tile
-constexpr int DT_NBUF = 4;
+constexpr int DT_NBUF = HD_DECODE_NBUF;
+static_assert(DT_NBUF >= 2 && DT_NBUF <= 5, "tile buffers");
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 
@@ -432,12 +440,12 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
     const int64_t tq_base = (int64_t)len * n;
 
     for (int t = 0; t < ntiles; ++t) {
-        // Tile t has landed; the (up to two) newer tiles already issued, 8
-        // copies each, may stay in flight.  gfx9 s_waitcnt immediates:
-        // 0x4F70 = vmcnt(16), 0x0F78 = vmcnt(8).
+        // Tile t has landed; the newer tiles already issued (8 copies each)
+        // may stay in flight (gfx9 s_waitcnt immediates).
         const int newer = min(ntiles - 1 - t, DT_NBUF - 2);
-        if (newer >= 2) __builtin_amdgcn_s_waitcnt(0x4F70);
-        else if (newer == 1) __builtin_amdgcn_s_waitcnt(0x0F78);
+        if (newer >= 3) __builtin_amdgcn_s_waitcnt(0x4F78);       // vmcnt(24)
+        else if (newer == 2) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+        else if (newer == 1) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
         else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // ... for every wave; tile t-1 fully consumed
         if (t + DT_NBUF - 1 < ntiles) issue(t + DT_NBUF - 1);
