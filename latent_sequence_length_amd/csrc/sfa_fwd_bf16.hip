@@ -209,7 +209,13 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 
 
 // ---------------------------------------------------------------------------
-// Head dim 128 fast path.  Same math and work decomposition as above, plus:
+// Head dim 128 fast path.  Same math as above, with these changes:
+//   * a workgroup is 8 waves (HG heads x 8/HG blocks of 32 positions), two
+//     per SIMD and one workgroup per CU, so every K/V tile copied into LDS
+//     serves 256 query rows (half the L2-to-LDS traffic of 4-wave groups);
+//   * each wave raises its issue priority while it issues the QK^T MFMAs, so
+//     the other wave of its SIMD fills the matrix core's gaps with its own
+//     softmax and PV rather than competing for it;
 //   * K and V tiles are fetched with direct-to-LDS 16-byte loads
 //     (global_load_lds), double-buffered: tile t+1 is in flight while tile t
 //     is computed, with no VGRPs spent on staging and one barrier per tile;
@@ -225,8 +231,7 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //     sums and bf16 P exact enough; the final normalisation is unchanged);
 //   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
 //     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
+constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
 
 // One tile of the d=128 loop: wait for tile `it` (in buffer `cur`), start
 // the DMA of tile it+1 into `nxt`, then compute tile `it`.  `cur` and `nxt`
@@ -255,6 +260,7 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
     const char *vbuf = cur + TILE;
 
     f32x16 sacc[2];
+    __builtin_amdgcn_s_setprio(1);  // the wave issuing MFMAs wins arbitration on its SIMD
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
         sacc[kb] = f32x16{};
@@ -268,6 +274,7 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
         }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     float mx = -INFINITY;
     if (need_mask) {
         // visible <=> lo <= key <= hi, checked as one unsigned compare
@@ -331,7 +338,7 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
     st.l_run += lsum;
 }
 
-__global__ __launch_bounds__(256, 2) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
+__global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
                                                                   float scale_log2) {
     constexpr int D = 128;
     constexpr int TILE = KT * D * 2;  // 16 KB per K or V tile
@@ -379,10 +386,11 @@ __global__ __launch_bounds__(256, 2) void sfa_fwd_bf16_d128_kernel(FwdArgs p, in
     // (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).  Rows past the end
     // of the sub-sequence re-read its last row (finite data, masked later).
     const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
-    int lrow[4], lchunk[4];
+    constexpr int PER = 16 / D128_NW;  // 1 KB copies of K (and of V) per wave per tile
+    int lrow[PER], lchunk[PER];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lrow[i] = (wave * 4 + i) * 4 + (lane >> 4);
+    for (int i = 0; i < PER; ++i) {
+        lrow[i] = (wave * PER + i) * 4 + (lane >> 4);
         lchunk[i] = ((lane & 15) ^ swz128(lrow[i])) * 8;
     }
     auto issue = [&](int t0, char *dst) {
@@ -390,9 +398,9 @@ __global__ __launch_bounds__(256, 2) void sfa_fwd_bf16_d128_kernel(FwdArgs p, in
         const bf16 *kt = kg + tbase, *vt = vg + tbase;
         const int rmax = p.Lsub - 1 - t0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < PER; ++i) {
             const int off = min(lrow[i], rmax) * rstride + lchunk[i];
-            const int s0 = (wave * 4 + i) * 64;
+            const int s0 = (wave * PER + i) * 64;
             lds_dma16(kt + off, lds_addr(dst + s0 * 16));
             lds_dma16(vt + off, lds_addr(dst + TILE + s0 * 16));
         }
@@ -461,13 +469,19 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
             hipLaunchKernelGGL(sfa_fwd_bf16_kernel<64>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk, sl2);
             break;
         case 128:
-            if ((int64_t)KT * a.stride * a.Hkv * 128 >= (int64_t)1 << 31) {  // 32-bit lane offsets
+            if ((int64_t)KT * a.stride * a.Hkv * 128 >= (int64_t)1 << 31) {  // 32-bit copy offsets
                 hipLaunchKernelGGL(sfa_fwd_bf16_kernel<128>, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk,
                                    sl2);
                 break;
             }
-            hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, HG, TB, nqblk,
-                               sl2);
+            {
+                const int TB2 = D128_NW / HG;
+                const int nqblk2 = (a.Lsub + QW * TB2 - 1) / (QW * TB2);
+                const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
+                if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+                hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid2), dim3(64 * D128_NW), 0, st, a, HG,
+                                   TB2, nqblk2, sl2);
+            }
             break;
         default:
             return hipErrorInvalidValue;
