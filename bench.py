@@ -8,11 +8,15 @@ are already resident in HBM:
   cross prefill  same shapes as the headline, dense causal over 16384 positions
   decode         64 sequences, 8192 cached tokens x 4 streams, 32 q / 8 kv heads,
                  intra and cross (one new token, 4 stream queries each)
+With --long, also the 32k-token layers (n=4, nL=131072, 16 q / 4 kv heads):
+intra-stream with a 4096-token window, local cross-stream with a 4096-token
+window, and a full cross-stream layer.
 Each call is timed with HIP events on the stream it is launched on.  The
 headline value is useful TFLOP/s of the intra-stream prefill (4*d*Hq FLOPs per
 visible query/key pair).  Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -24,8 +28,43 @@ import torch
 
 from latent_sequence_length_amd import hd, synth
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def useful_flops(B, L, n, Hq, d, mode, window=0):
+    """4*d*Hq*(number of visible (query, key) pairs): QK^T and PV, 2 flops per
+    multiply-add.  Intra: per stream, tokens j <= i within the window; cross:
+    positions t_k <= t_q within n*window positions."""
+    def tri(T, w):  # sum over q in [0, T) of min(q + 1, w) (w = 0: no window)
+        if w <= 0 or w >= T:
+            return T * (T + 1) // 2
+        return w * (w + 1) // 2 + (T - w) * w
+    pairs = n * tri(L, window) if mode == 0 else tri(n * L, n * window)
+    return 4.0 * d * Hq * B * pairs
+
+
+def measured_traffic(name):
+    """HBM bytes per launch of a kernel from its committed PMC summary
+    (profiles/<name>.md: FETCH_SIZE + WRITE_SIZE scaled by a copy kernel), or
+    None when the summary is missing or the kernel source has changed since
+    the counters were taken (the summary records the source's SHA-256)."""
+    path = os.path.join(ROOT, "profiles", name + ".md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- `"):
+            key, val = line[3:].split("`:", 1)
+            fields[key.strip()] = val.strip().strip("`")
+    src = fields.get("source")
+    if not src or "traffic_bytes_per_launch" not in fields:
+        return None
+    digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    if digest != fields.get("source_sha256"):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def parse():
@@ -114,24 +153,21 @@ def main():
 
     comps = {}   # name -> (callable, useful flops, algorithmic bytes)
 
-    if want("intra_n4"):
-        q, k, v = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+    def prefill(cfg):
+        """(callable, useful flops, algorithmic bytes) of one prefill call on
+        inputs drawn once; bytes = q, k, v read + o written."""
+        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
         o = torch.empty_like(q)
-        fl = synth.useful_flops(I.B, I.L, I.n, I.Hq, I.d, 0)
+        fl = useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
         by = 2 * (2 * q.numel() + k.numel() + v.numel())
-        comps["intra_n4"] = (lambda q=q, k=k, v=v, o=o: hd.hd_sfa_fwd(q, k, v, o, I.n, 0), fl, by)
+        return (lambda: hd.hd_sfa_fwd(q, k, v, o, cfg.n, cfg.mode, cfg.window), fl, by)
+
+    if want("intra_n4"):
+        comps["intra_n4"] = prefill(I)
     if want("intra_n1"):
-        q1, k1, v1 = synth.qkv(I1.B, I1.L, I1.n, I1.Hq, I1.Hkv, I1.d, I1.dtype, dev)
-        o1 = torch.empty_like(q1)
-        fl = synth.useful_flops(I1.B, I1.L, I1.n, I1.Hq, I1.d, 0)
-        by = 2 * (2 * q1.numel() + k1.numel() + v1.numel())
-        comps["intra_n1"] = (lambda: hd.hd_sfa_fwd(q1, k1, v1, o1, I1.n, 0), fl, by)
+        comps["intra_n1"] = prefill(I1)
     if want("cross_n4"):
-        qx, kx, vx = synth.qkv(X.B, X.L, X.n, X.Hq, X.Hkv, X.d, X.dtype, dev)
-        ox = torch.empty_like(qx)
-        fl = synth.useful_flops(X.B, X.L, X.n, X.Hq, X.d, 1)
-        by = 2 * (2 * qx.numel() + kx.numel() + vx.numel())
-        comps["cross_n4"] = (lambda: hd.hd_sfa_fwd(qx, kx, vx, ox, X.n, 1), fl, by)
+        comps["cross_n4"] = prefill(X)
     if want("decode_intra") or want("decode_cross"):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)
@@ -169,14 +205,17 @@ def main():
         by = 2 * eo.numel() * 2 + E["B"] * E["L"] * 4
         comps["embed"] = (run_embed, 0.0, by)
     if args.long:
-        for cfg, name in ((synth.LONG_INTRA_W, "long_intra_w4096"), (synth.LONG_CROSS, "long_cross")):
+        for cfg, name in ((synth.LONG_INTRA_W, "long_intra_w4096"), (synth.LONG_CROSS_W, "long_cross_w4096"),
+                          (synth.LONG_CROSS, "long_cross")):
             if want(name):
-                ql, kl, vl = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
-                ol = torch.empty_like(ql)
-                fl = synth.useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
-                by = 2 * (2 * ql.numel() + kl.numel() + vl.numel())
-                comps[name] = (lambda ql=ql, kl=kl, vl=vl, ol=ol, cfg=cfg:
-                               hd.hd_sfa_fwd(ql, kl, vl, ol, cfg.n, cfg.mode, cfg.window), fl, by)
+                comps[name] = prefill(cfg)
+    if "copy" in only:
+        # calibration only, never part of the step: a plain elementwise copy
+        # of 512 MiB, which reads and writes exactly that many bytes; its HBM
+        # byte counters scale the counters of the kernels above
+        src = torch.randn(256 << 20, device=dev).to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        comps["copy"] = (lambda: torch.mul(src, 1.0, out=dst), 0.0, 2 * src.numel() * 2)
     torch.cuda.synchronize()
 
     timer = Timer()
@@ -214,7 +253,8 @@ def main():
         fl = comps["intra_n4"][1]
         ach = fl / report["intra_n4"]["ms"] / 1e9
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic("sfa_fwd_bf16_d128__intra_n4_L4096__hbm_bytes"),
                 "kernel": "sfa_fwd_bf16_d128_kernel", "per_launch_flops": fl}
     roof_dec = None
     if "decode_intra" in report:
@@ -222,6 +262,7 @@ def main():
         ach = by / report["decode_intra"]["ms"] / 1e6
         roof_dec = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": round(ach / PEAK_HBM_GBPS, 4), "per_launch_bytes": by,
+                    "traffic": measured_traffic("sfa_decode_d128__intra_B64_ctx8192__hbm_bytes"),
                     "kernels": "decode_partial_d128_kernel<1> + decode_combine_kernel<128>"}
 
     line = {

@@ -99,23 +99,8 @@ INTRA_4K_N1 = PrefillShape("intra n1 L4096 32q/8kv d128 bf16", 1, 4096, 1, 32, 8
 CROSS_4K = PrefillShape("cross n4 L4096 32q/8kv d128 bf16", 1, 4096, 4, 32, 8, 128, 1, 0, torch.bfloat16)
 LONG_INTRA_W = PrefillShape("intra-W4096 n4 L32768 16q/4kv d128 bf16", 1, 32768, 4, 16, 4, 128, 0, 4096, torch.bfloat16)
 LONG_CROSS = PrefillShape("cross n4 L32768 16q/4kv d128 bf16", 1, 32768, 4, 16, 4, 128, 1, 0, torch.bfloat16)
+LONG_CROSS_W = PrefillShape("cross-W4096 n4 L32768 16q/4kv d128 bf16", 1, 32768, 4, 16, 4, 128, 1, 4096, torch.bfloat16)
 DECODE_8K = DecodeShape("decode B64 ctx8192 n4 32q/8kv d128 bf16", 64, 8192, 4, 32, 8, 128, torch.bfloat16)
 EMBED_DECODE = dict(B=64, L=1, n=4, V=160000, D=7168, dtype=torch.bfloat16)
 EMBED_PREFILL = dict(B=1, L=4096, n=4, V=160000, D=7168, dtype=torch.bfloat16)
 
-
-def useful_flops(B, L, n, Hq, d, mode, window=0):
-    """4*d*Hq*(number of visible (query, key) pairs): QK^T and PV, 2 flops/MAC.
-
-    Counting only; the visible-pair count follows the mask definitions (intra:
-    per stream, tokens j <= i within the window; cross: positions t_k <= t_q
-    within n*window)."""
-    def tri(T, w):  # sum over q in [0,T) of min(q+1, w) (w = 0: no window)
-        if w <= 0 or w >= T:
-            return T * (T + 1) // 2
-        return w * (w + 1) // 2 + (T - w) * w
-    if mode == 0:
-        pairs = n * tri(L, window)
-    else:
-        pairs = tri(n * L, n * window)
-    return 4.0 * d * Hq * B * pairs

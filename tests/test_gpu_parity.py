@@ -188,7 +188,7 @@ def sample_rows(B, L, n, Hq, window, count, seed):
     return np.unique(np.array(rows, dtype=np.int64))
 
 
-FULL = [synth.INTRA_4K, synth.INTRA_4K_N1, synth.CROSS_4K, synth.LONG_INTRA_W, synth.LONG_CROSS]
+FULL = [synth.INTRA_4K, synth.INTRA_4K_N1, synth.CROSS_4K, synth.LONG_INTRA_W, synth.LONG_CROSS_W, synth.LONG_CROSS]
 
 
 @pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
