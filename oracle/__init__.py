@@ -17,8 +17,11 @@ Designs"): the expansion equation S_t = E_k(x_i) with t = (i-1)n + k; the index
 maps i(t) = ceil(t/n), s(t) = (t-1) mod n + 1 and Figure 2's three masks; the
 per-stream KV cache retained for decoding.
 
+The backward (``sfa_bwd*``) is the chain-rule derivative of that forward.
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against library
-routines, closed forms, invariants and hand-worked golden values.
+routines, closed forms, invariants, finite differences and hand-worked golden
+values.
 """
 import ctypes
 import os
@@ -58,8 +61,9 @@ def _configure(lib):
     lib.oracle_sfa_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
     lib.oracle_sfa_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, I64, D, P]
     lib.oracle_decode_append.argtypes = [P, P, P, I, I, I, I, I, I64]
+    lib.oracle_sfa_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P, P, I64, P, P, I64, P, P]
     for f in (lib.oracle_expand_embed, lib.oracle_visible, lib.oracle_sfa_rows,
-              lib.oracle_sfa_fwd, lib.oracle_sfa_decode, lib.oracle_decode_append):
+              lib.oracle_sfa_fwd, lib.oracle_sfa_decode, lib.oracle_decode_append, lib.oracle_sfa_bwd_rows):
         f.restype = ctypes.c_int
     return lib
 
@@ -191,3 +195,54 @@ def decode_append(x_new, cache, cache_len):
     if rc:
         raise ValueError("cache_len outside [0, T_cap)")
     return out
+
+
+def row_stats(q, k, v, dout, n, mode, window=0, scale=0.0):
+    """Per query row softmax normaliser lse and D = dO . O, both [B, Hq, nL]
+    float64, from the forward definition (``sfa_fwd``)."""
+    o, lse = sfa_fwd(q, k, v, n, mode, window, scale)
+    db, _ = _buf(dout)
+    dbl = db.astype(np.float64) if db.dtype == np.float32 else _bf16_to_f64(db)
+    D = np.einsum("btHc,btHc->bHt", dbl, o)
+    return np.ascontiguousarray(lse), np.ascontiguousarray(D)
+
+
+def _bf16_to_f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def sfa_bwd_rows(q, k, v, dout, n, mode, window=0, scale=0.0, qrows=None, krows=None, stats=None):
+    """Gradients of sum(dO * O): dq for flat query rows (b*nL+t)*Hq+h and dk, dv
+    for flat key rows (b*nL+t)*Hkv+hk (float64 arrays [rows, d]).  stats =
+    (lse, D) from ``row_stats`` (computed here when None)."""
+    qb, dt = _buf(q)
+    kb, _ = _buf(k)
+    vb, _ = _buf(v)
+    db, dt2 = _buf(dout)
+    if dt != dt2:
+        raise TypeError("dout must share q's dtype")
+    B, nL, Hq, d = qb.shape
+    Hkv = kb.shape[2]
+    if stats is None:
+        stats = row_stats(q, k, v, dout, n, mode, window, scale)
+    lse, D = (np.ascontiguousarray(x, dtype=np.float64) for x in stats)
+    qrows = np.ascontiguousarray(np.asarray([] if qrows is None else qrows, dtype=np.int64))
+    krows = np.ascontiguousarray(np.asarray([] if krows is None else krows, dtype=np.int64))
+    dq = np.empty((qrows.size, d))
+    dk = np.empty((krows.size, d))
+    dv = np.empty((krows.size, d))
+    rc = _load().oracle_sfa_bwd_rows(_p(qb), _p(kb), _p(vb), _p(db), dt, B, nL // n, n, Hq, Hkv, d,
+                                     int(mode), int(window), float(scale), _p(lse), _p(D),
+                                     _p(qrows), qrows.size, _p(dq), _p(krows), krows.size, _p(dk), _p(dv))
+    if rc:
+        raise ValueError("oracle_sfa_bwd_rows rejected its arguments")
+    return dq, dk, dv
+
+
+def sfa_bwd(q, k, v, dout, n, mode, window=0, scale=0.0):
+    """Full backward: dq [B, nL, Hq, d], dk / dv [B, nL, Hkv, d] (float64)."""
+    B, nL, Hq, d = tuple(q.shape)
+    Hkv = tuple(k.shape)[2]
+    dq, dk, dv = sfa_bwd_rows(q, k, v, dout, n, mode, window, scale,
+                              qrows=np.arange(B * nL * Hq), krows=np.arange(B * nL * Hkv))
+    return dq.reshape(B, nL, Hq, d), dk.reshape(B, nL, Hkv, d), dv.reshape(B, nL, Hkv, d)

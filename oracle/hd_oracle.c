@@ -270,3 +270,87 @@ int oracle_decode_append(const void *x_new, void *cache, const int32_t *cache_le
     }
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Backward of the prefill attention: the gradient of the scalar
+ * sum_{b,t,h,c} dO[b][t][h][c] * O[b][t][h][c] with respect to Q, K and V,
+ * written out from the definition of O above by the chain rule.  For a query
+ * row (b, t, h) with visible keys j (Figure 2's mask), softmax weights
+ * p_j = exp(scale * q.k_j - lse) and D = dO . O:
+ *   dP_j  = dO . v_j
+ *   dS_j  = p_j * (dP_j - D)                 (softmax Jacobian applied to dP)
+ *   dQ   += scale * sum_j dS_j k_j
+ *   dK_j += scale * dS_j q         (summed over the query heads of the group)
+ *   dV_j += p_j dO                 (summed over the query heads of the group)
+ * The pages define the forward only; this derivative is the textbook one of
+ * that forward (nothing is approximated).
+ *
+ * lse and Drow ([B][Hq][nL], double) are the forward's softmax normaliser and
+ * dO . O of every query row (from oracle_sfa_fwd).  qrows selects flat query
+ * rows (b*nL + t)*Hq + h for dq [nq][d]; krows selects flat key rows
+ * (b*nL + t)*Hkv + hk for dk, dv [nk][d].  Keys and queries are visited in
+ * ascending position order; every sum is in double.  Returns 0 or -1.
+ * ------------------------------------------------------------------------- */
+int oracle_sfa_bwd_rows(const void *q, const void *k, const void *v, const void *dout, int dtype,
+                        int B, int L, int n, int Hq, int Hkv, int d, int mode, int64_t W,
+                        double scale, const double *lse, const double *Drow,
+                        const int64_t *qrows, int64_t nq, double *dq,
+                        const int64_t *krows, int64_t nk, double *dk, double *dv) {
+    if (B < 1 || L < 1 || n < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv) return -1;
+    if (W < 0 || (mode != OR_INTRA && mode != OR_CROSS)) return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    const int64_t nL = (int64_t)n * L;
+    const int g = Hq / Hkv;
+    int bad = 0;
+    /* dQ rows */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t r = 0; r < nq; ++r) {
+        int64_t id = qrows[r];
+        if (id < 0 || id >= (int64_t)B * nL * Hq) { bad = 1; continue; }
+        int64_t h = id % Hq, t = (id / Hq) % nL, b = id / Hq / nL, hk = h / g;
+        double lse_t = lse[(b * Hq + h) * nL + t], D_t = Drow[(b * Hq + h) * nL + t];
+        double *out = dq + r * d;
+        for (int c = 0; c < d; ++c) out[c] = 0.0;
+        for (int64_t tk = 0; tk <= t; ++tk) {
+            if (!oracle_visible(t, tk, n, mode, W)) continue;
+            int64_t koff = ((b * nL + tk) * Hkv + hk) * d;
+            double s = 0.0, dp = 0.0;
+            for (int c = 0; c < d; ++c) {
+                s += load_elem(q, dtype, id * d + c) * load_elem(k, dtype, koff + c);
+                dp += load_elem(dout, dtype, id * d + c) * load_elem(v, dtype, koff + c);
+            }
+            double p = exp(scale * s - lse_t);
+            double ds = p * (dp - D_t);
+            for (int c = 0; c < d; ++c) out[c] += scale * ds * load_elem(k, dtype, koff + c);
+        }
+    }
+    /* dK, dV rows */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t r = 0; r < nk; ++r) {
+        int64_t id = krows[r];
+        if (id < 0 || id >= (int64_t)B * nL * Hkv) { bad = 1; continue; }
+        int64_t hk = id % Hkv, tk = (id / Hkv) % nL, b = id / Hkv / nL;
+        double *gk = dk + r * d, *gv = dv + r * d;
+        for (int c = 0; c < d; ++c) gk[c] = gv[c] = 0.0;
+        for (int hh = 0; hh < g; ++hh) {
+            int64_t h = hk * g + hh;
+            for (int64_t t = tk; t < nL; ++t) {
+                if (!oracle_visible(t, tk, n, mode, W)) continue;
+                int64_t qoff = ((b * nL + t) * Hq + h) * d;
+                double lse_t = lse[(b * Hq + h) * nL + t], D_t = Drow[(b * Hq + h) * nL + t];
+                double s = 0.0, dp = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    s += load_elem(q, dtype, qoff + c) * load_elem(k, dtype, id * d + c);
+                    dp += load_elem(dout, dtype, qoff + c) * load_elem(v, dtype, id * d + c);
+                }
+                double p = exp(scale * s - lse_t);
+                double ds = p * (dp - D_t);
+                for (int c = 0; c < d; ++c) {
+                    gk[c] += scale * ds * load_elem(q, dtype, qoff + c);
+                    gv[c] += p * load_elem(dout, dtype, qoff + c);
+                }
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}

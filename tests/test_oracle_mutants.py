@@ -43,6 +43,18 @@ MUTANTS = [
      [lambda o: pins.test_decode_equals_prefill_rows(o, CROSS, 0)]),
     ("expansion stream-major", "(((int64_t)b * L + i) * n + s) * row_bytes",
      "(((int64_t)b * n + s) * L + i) * row_bytes", [pins.test_expand_golden_order]),
+    ("bwd dQ accumulates value rows", "out[c] += scale * ds * load_elem(k, dtype, koff + c);",
+     "out[c] += scale * ds * load_elem(v, dtype, koff + c);",
+     [lambda o: pins.test_bwd_matches_autograd(o, CROSS, 0, 1),
+      lambda o: pins.test_bwd_finite_differences(o, INTRA, 0)]),
+    ("bwd dK drops the scale", "gk[c] += scale * ds * load_elem(q, dtype, qoff + c);",
+     "gk[c] += ds * load_elem(q, dtype, qoff + c);",
+     [lambda o: pins.test_bwd_matches_autograd(o, INTRA, 2, 2)]),
+    ("bwd dV weighted by dS", "gv[c] += p * load_elem(dout, dtype, qoff + c);",
+     "gv[c] += ds * load_elem(dout, dtype, qoff + c);",
+     [lambda o: pins.test_bwd_invariants(o, CROSS, 0), pins.test_bwd_zero_query_closed_form]),
+    ("bwd key rows skip their own query", "for (int64_t t = tk; t < nL; ++t) {",
+     "for (int64_t t = tk + 1; t < nL; ++t) {", [pins.test_bwd_window1_closed_form]),
 ]
 
 

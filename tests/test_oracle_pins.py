@@ -351,3 +351,121 @@ def test_decode_append_bytes(oracle):
     np.testing.assert_array_equal(out, want.view(torch.int16).numpy().view(np.uint16))
     with pytest.raises(ValueError):
         oracle.decode_append(kn, kc, [0, 5, 1])
+
+
+# --------------------------------------------------------------------------
+# Backward (gradient of sum(dO * O)); the forward's chain-rule derivative
+# --------------------------------------------------------------------------
+
+def _bwd_inputs(B, L, n, Hq, Hkv, d, seed=0):
+    q = _rand((B, n * L, Hq, d), 10 + seed)
+    k = _rand((B, n * L, Hkv, d), 20 + seed)
+    v = _rand((B, n * L, Hkv, d), 30 + seed)
+    do = _rand((B, n * L, Hq, d), 40 + seed)
+    return q, k, v, do
+
+
+def autograd_bwd(q, k, v, do, n, mode, W, scale=None):
+    """torch float64 autograd of masked softmax attention (explicit Figure 2
+    mask from the 1-based index maps, GQA by repeating K/V)."""
+    L = q.shape[1] // n
+    m = torch.from_numpy(brute.mask(n, L, mode, W))
+    q64, k64, v64 = (x.double().requires_grad_(True) for x in (q, k, v))
+    out = sdpa64(q64, k64, v64, attn_mask=m, scale=scale)
+    (out * do.double()).sum().backward()
+    return q64.grad.numpy(), k64.grad.numpy(), v64.grad.numpy()
+
+
+@pytest.mark.parametrize("mode,W,g", [(INTRA, 0, 1), (CROSS, 0, 1), (INTRA, 2, 2), (CROSS, 3, 2),
+                                      (INTRA, 0, 4), (CROSS, 0, 3)])
+def test_bwd_matches_autograd(oracle, mode, W, g):
+    B, L, n, Hkv, d = 2, 7, 3, 2, 16
+    q, k, v, do = _bwd_inputs(B, L, n, g * Hkv, Hkv, d, seed=mode + W + g)
+    dq, dk, dv = oracle.sfa_bwd(q, k, v, do, n, mode, W)
+    wq, wk, wv = autograd_bwd(q, k, v, do, n, mode, W)
+    np.testing.assert_allclose(dq, wq, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dk, wk, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dv, wv, rtol=1e-9, atol=1e-11)
+
+
+def test_bwd_custom_scale_matches_autograd(oracle):
+    q, k, v, do = _bwd_inputs(1, 6, 2, 2, 1, 8, seed=5)
+    dq, dk, dv = oracle.sfa_bwd(q, k, v, do, 2, CROSS, 0, scale=0.3)
+    wq, wk, wv = autograd_bwd(q, k, v, do, 2, CROSS, 0, scale=0.3)
+    for got, want in ((dq, wq), (dk, wk), (dv, wv)):
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 2)])
+def test_bwd_finite_differences(oracle, mode, W):
+    """Central differences of sum(dO * O) through the forward oracle only."""
+    B, L, n, Hq, Hkv, d = 1, 3, 2, 2, 1, 4
+    q, k, v, do = _bwd_inputs(B, L, n, Hq, Hkv, d, seed=7)
+    dq, dk, dv = oracle.sfa_bwd(q, k, v, do, n, mode, W)
+    h = 2.0 ** -12   # exactly representable; inputs stay float32
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.sfa_fwd(qq, kk, vv, n, mode, W)
+        return float((o * do.double().numpy()).sum())
+
+    rng = np.random.default_rng(3)
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = [q, k, v]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(s)) for s in base[which].shape)
+            plus = [x.clone() for x in base]
+            minus = [x.clone() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd = (loss(*plus) - loss(*minus)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 2e-5 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+def test_bwd_window1_closed_form(oracle):
+    """Intra, W=1: each query sees only itself, so O = V, dQ = dK = 0 and
+    dV[t, hk] = sum of dO[t, h] over the heads of the group."""
+    B, L, n, Hq, Hkv, d = 1, 5, 3, 4, 2, 8
+    q, k, v, do = _bwd_inputs(B, L, n, Hq, Hkv, d, seed=11)
+    dq, dk, dv = oracle.sfa_bwd(q, k, v, do, n, INTRA, 1)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    want = do.double().numpy().reshape(B, n * L, Hkv, Hq // Hkv, d).sum(axis=3)
+    np.testing.assert_allclose(dv, want, rtol=1e-12, atol=1e-13)
+
+
+def test_bwd_zero_query_closed_form(oracle):
+    """Q = 0: uniform weights over the visible keys, so dV_j = sum over the
+    queries i that see j of dO_i / (number of keys i sees)."""
+    B, L, n, Hq, Hkv, d = 1, 6, 2, 2, 1, 4
+    _, k, v, do = _bwd_inputs(B, L, n, Hq, Hkv, d, seed=13)
+    q = torch.zeros(B, n * L, Hq, d)
+    for mode in (INTRA, CROSS):
+        m = brute.mask(n, L, mode, 0)
+        _, _, dv = oracle.sfa_bwd(q, k, v, do, n, mode, 0)
+        w = m / m.sum(axis=1, keepdims=True)          # [tq, tk]
+        dosum = do.double().numpy()[0].sum(axis=1)      # heads of the single group
+        want = w.T @ dosum
+        np.testing.assert_allclose(dv[0, :, 0], want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (CROSS, 4), (INTRA, 3)])
+def test_bwd_invariants(oracle, mode, W):
+    """Softmax rows sum to one: summed over all keys, dK vanishes and dV
+    equals the sum of dO over the group's heads and all positions."""
+    B, L, n, Hq, Hkv, d = 2, 9, 4, 4, 2, 8
+    q, k, v, do = _bwd_inputs(B, L, n, Hq, Hkv, d, seed=17)
+    _, dk, dv = oracle.sfa_bwd(q, k, v, do, n, mode, W)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-10
+    want = do.double().numpy().reshape(B, n * L, Hkv, Hq // Hkv, d).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), want, rtol=1e-10, atol=1e-10)
+
+
+def test_bwd_rows_subset_matches_full(oracle):
+    B, L, n, Hq, Hkv, d = 1, 8, 2, 4, 2, 16
+    q, k, v, do = _bwd_inputs(B, L, n, Hq, Hkv, d, seed=19)
+    dq, dk, dv = oracle.sfa_bwd(q, k, v, do, n, CROSS, 3)
+    qrows = np.array([0, 5, 17, 40, B * n * L * Hq - 1])
+    krows = np.array([0, 3, 11, B * n * L * Hkv - 1])
+    sq, sk, sv = oracle.sfa_bwd_rows(q, k, v, do, n, CROSS, 3, qrows=qrows, krows=krows)
+    np.testing.assert_array_equal(sq, dq.reshape(-1, d)[qrows])
+    np.testing.assert_array_equal(sk, dk.reshape(-1, d)[krows])
+    np.testing.assert_array_equal(sv, dv.reshape(-1, d)[krows])
