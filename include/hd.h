@@ -93,6 +93,38 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
                      hd_mode mode, int window, float scale, hd_dtype dt, void *stream);
 
 /*
+ * Bytes of device workspace hd_sfa_bwd needs for these sizes (0 if the sizes
+ * are invalid): one float32 per query row, B*Hq*n*L*4.
+ */
+size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt);
+
+/*
+ * Backward of hd_sfa_fwd: the gradients of the scalar sum(dout * o) with
+ * respect to q, k and v, for the same mask, window and scale.  The pages
+ * define the forward ("Stream-Factorized Attention", Figure 2) and state the
+ * method's cost in training step time ("Near-Linear Training Cost", Figure 3);
+ * this is the standard derivative of that forward.  With P the softmax
+ * weights over the visible keys (recomputed from lse) and D = dout . o per
+ * query row:
+ *   dP = dout . v,  dS = P * (dP - D)
+ *   dq = scale * dS k,   dk = scale * dS^T q,   dv = P^T dout
+ * where dk and dv sum over the query heads of each kv head's GQA group.
+ *   q, o, dout, dq  [B][n*L][Hq][d]      k, v, dk, dv  [B][n*L][Hkv][d]  (dtype dt)
+ *   lse        float32 [B][Hq][n*L] as written by hd_sfa_fwd for these inputs
+ *   workspace  device, >= hd_sfa_bwd_workspace_bytes(...) bytes; contents on
+ *              entry do not matter; two calls that may run concurrently need
+ *              separate workspaces
+ * Every output element is written exactly once (no atomics); results are
+ * deterministic.  Size rules as for hd_sfa_fwd; all pointers must be non-NULL
+ * and 16-byte aligned.
+ */
+hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *dq, void *dk, void *dv,
+                     int B, int L, int n, int Hq, int Hkv, int d,
+                     hd_mode mode, int window, float scale, hd_dtype dt,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace hd_sfa_decode needs for these sizes (0 if the
  * sizes are invalid).  The workspace holds float32 split-KV partial results.
  */

@@ -132,6 +132,50 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
     return device_status(e, "sfa_fwd launch");
 }
 
+size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
+    if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
+    if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;
+    return hd::bwd_workspace_bytes(B, n * L, Hq);
+}
+
+hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq, int Hkv, int d,
+                     hd_mode mode, int window, float scale, hd_dtype dt, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
+    HD_TRY(check_ptr(q, "q"));
+    HD_TRY(check_ptr(k, "k"));
+    HD_TRY(check_ptr(v, "v"));
+    HD_TRY(check_ptr(o, "o"));
+    HD_TRY(check_ptr(dout, "dout"));
+    HD_TRY(check_ptr(dq, "dq"));
+    HD_TRY(check_ptr(dk, "dk"));
+    HD_TRY(check_ptr(dv, "dv"));
+    HD_TRY(check_ptr(lse, "lse"));
+    HD_TRY(check_ptr(workspace, "workspace"));
+    const size_t need = hd::bwd_workspace_bytes(B, n * L, Hq);
+    if (workspace_bytes < need)
+        return fail(HD_ERR_INVALID, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    hd::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.drow = static_cast<float *>(workspace);
+    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    if (mode == HD_MODE_INTRA) {
+        a.Lsub = L; a.nsub = n; a.stride = n;
+        a.weff = window >= L ? 0 : window;
+    } else {
+        a.Lsub = n * L; a.nsub = 1; a.stride = 1;
+        const int64_t w = (int64_t)n * window;
+        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
+    }
+    a.scale = resolve_scale(scale, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_bwd_bf16(a, st) : hd::launch_sfa_bwd_f32(a, st);
+    return device_status(e, "sfa_bwd launch");
+}
+
 size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap) {
     if (B < 1 || n < 1 || Hq < 1 || Hkv < 1 || d < 1 || T_cap < 1 || Hq % Hkv) return 0;
     return hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);

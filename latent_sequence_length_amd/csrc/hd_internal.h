@@ -52,6 +52,21 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Backward of the prefill, in the same sub-sequence form as FwdArgs.
+struct BwdArgs {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;  // [B][Hq][nL], natural log, from the forward
+    void *dq, *dk, *dv;
+    float *drow;       // workspace [B][Hq][nL]: D = dO . O per query row
+    int B, nL, Hq, Hkv, d;
+    int Lsub, nsub, stride, weff;
+    float scale;
+};
+size_t bwd_workspace_bytes(int B, int nL, int Hq);
+hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st);
+hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Decode over the per-stream cache [B][T_cap][n][Hkv][d].
 struct DecArgs {
     const void *q, *k_new, *v_new;

@@ -1,0 +1,491 @@
+// sfa_bwd.hip -- backward of Stream-Factorized Attention prefill: dQ, dK, dV
+// of the scalar sum(dO * O), for bf16 (matrix cores, fp32 accumulation) and
+// float32 (vector ALUs, exactness checks).
+//
+// The pages define the forward ("Hidden Decoding at Scale", "Stream-Factorized
+// Attention", Figure 2 masks); training through it needs the derivative of
+// that forward, which is the standard one of masked softmax attention.  For a
+// query row i with visible keys j, P_ij = exp(scale q_i.k_j - lse_i) (lse from
+// the forward) and D_i = dO_i . O_i:
+//   dP_ij = dO_i . v_j,   dS_ij = P_ij (dP_ij - D_i)
+//   dQ_i  = scale sum_j dS_ij k_j
+//   dK_j  = scale sum_i dS_ij q_i,   dV_j = sum_i P_ij dO_i
+// where the sums over i run over the query heads of the kv head's GQA group.
+// Both masks use the strided sub-sequence form of FwdArgs: intra-stream
+// attention is n independent causal attentions on the streams, cross-stream
+// one causal attention over all positions.
+//
+// Three launches, no atomics, every output element written once:
+//   1. D_i = dO_i . O_i for every query row (fp32, into the workspace);
+//   2. dK, dV: a workgroup owns 128 keys of one (batch, kv head, sub-sequence)
+//      and walks the query tiles (all heads of the group) that see them;
+//   3. dQ: a wave owns 32 queries of one head and walks the key tiles they see
+//      (the forward's loop, recomputing P from lse).
+#include "attn_common.h"
+
+namespace hd {
+
+namespace {
+
+constexpr int BKT = 64;   // keys per tile (dQ kernel)
+constexpr int BQT = 32;   // queries per tile (dK/dV kernel)
+constexpr int BKW = 128;  // keys per workgroup (dK/dV kernel)
+
+// ---------------------------------------------------------------------------
+// 1. D = dO . O per query row; 16 lanes per row, fp32.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void bwd_drow_kernel(BwdArgs p) {
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b*nL + t)*Hq + h
+    const int part = threadIdx.x & 15;
+    const int64_t nrows = (int64_t)p.B * p.nL * p.Hq;
+    constexpr int PER = D / 16;
+    float acc = 0.f;
+    if (row < nrows) {
+        const T *o = static_cast<const T *>(p.o) + row * D + part * PER;
+        const T *g = static_cast<const T *>(p.dout) + row * D + part * PER;
+#pragma unroll
+        for (int c = 0; c < PER; ++c) acc = fmaf((float)o[c], (float)g[c], acc);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (row < nrows && part == 0) {
+        const int64_t h = row % p.Hq, t = (row / p.Hq) % p.nL, b = row / p.Hq / p.nL;
+        p.drow[(b * p.Hq + h) * p.nL + t] = acc;
+    }
+}
+
+// Row (b, sub, j) of the sub-sequence form -> expanded position.
+__device__ __forceinline__ int64_t sub_pos(const BwdArgs &p, int b, int sub, int j) {
+    return (int64_t)b * p.nL + sub + (int64_t)j * p.stride;
+}
+
+// Index of a query row's lse / D entry: [b][h][position within the batch row].
+__device__ __forceinline__ int64_t row_stat(const BwdArgs &p, int b, int h, int64_t pos) {
+    return ((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL);
+}
+
+// ---------------------------------------------------------------------------
+// float32: one thread per query row (dQ) or per key row (dK, dV).
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs p) {
+    const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, sub, i, h)
+    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lsub * p.Hq;
+    if (row >= nrows) return;
+    const int h = (int)(row % p.Hq);
+    int64_t r = row / p.Hq;
+    const int i = (int)(r % p.Lsub); r /= p.Lsub;
+    const int sub = (int)(r % p.nsub);
+    const int b = (int)(r / p.nsub);
+    const int kvh = h / (p.Hq / p.Hkv);
+    const int64_t pos = sub_pos(p, b, sub, i);
+    const float *qp = static_cast<const float *>(p.q) + (pos * p.Hq + h) * D;
+    const float *gp = static_cast<const float *>(p.dout) + (pos * p.Hq + h) * D;
+    const float *kg = static_cast<const float *>(p.k);
+    const float *vg = static_cast<const float *>(p.v);
+    float qv[D], gv[D], acc[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) { qv[c] = qp[c]; gv[c] = gp[c]; acc[c] = 0.f; }
+    const float lse = p.lse[row_stat(p, b, h, pos)], Dr = p.drow[row_stat(p, b, h, pos)];
+    const int jbeg = p.weff ? max(0, i - p.weff + 1) : 0;
+    for (int j = jbeg; j <= i; ++j) {
+        const int64_t off = (sub_pos(p, b, sub, j) * p.Hkv + kvh) * D;
+        float s = 0.f, dp = 0.f;
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+            s = fmaf(qv[c], kg[off + c], s);
+            dp = fmaf(gv[c], vg[off + c], dp);
+        }
+        const float ds = expf(s * p.scale - lse) * (dp - Dr);
+#pragma unroll
+        for (int c = 0; c < D; ++c) acc[c] = fmaf(ds, kg[off + c], acc[c]);
+    }
+    float *out = static_cast<float *>(p.dq) + (pos * p.Hq + h) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) out[c] = p.scale * acc[c];
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdArgs p) {
+    __shared__ float ks[64][D + 1], vs[64][D + 1];  // this thread's key / value row
+    const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, sub, j, kvh)
+    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lsub * p.Hkv;
+    if (row >= nrows) return;
+    const int kvh = (int)(row % p.Hkv);
+    int64_t r = row / p.Hkv;
+    const int j = (int)(r % p.Lsub); r /= p.Lsub;
+    const int sub = (int)(r % p.nsub);
+    const int b = (int)(r / p.nsub);
+    const int g = p.Hq / p.Hkv;
+    const int64_t kpos = sub_pos(p, b, sub, j);
+    const float *kr = static_cast<const float *>(p.k) + (kpos * p.Hkv + kvh) * D;
+    const float *vr = static_cast<const float *>(p.v) + (kpos * p.Hkv + kvh) * D;
+    float *myk = ks[threadIdx.x], *myv = vs[threadIdx.x];
+    for (int c = 0; c < D; ++c) { myk[c] = kr[c]; myv[c] = vr[c]; }
+    float ak[D], av[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) ak[c] = av[c] = 0.f;
+    const int iend = p.weff ? min(p.Lsub - 1, j + p.weff - 1) : p.Lsub - 1;
+    for (int hh = 0; hh < g; ++hh) {
+        const int h = kvh * g + hh;
+        for (int i = j; i <= iend; ++i) {
+            const int64_t qpos = sub_pos(p, b, sub, i);
+            const float *qp = static_cast<const float *>(p.q) + (qpos * p.Hq + h) * D;
+            const float *gp = static_cast<const float *>(p.dout) + (qpos * p.Hq + h) * D;
+            float s = 0.f, dp = 0.f;
+            for (int c = 0; c < D; ++c) {
+                s = fmaf(qp[c], myk[c], s);
+                dp = fmaf(gp[c], myv[c], dp);
+            }
+            const float pr = expf(s * p.scale - p.lse[row_stat(p, b, h, qpos)]);
+            const float ds = pr * (dp - p.drow[row_stat(p, b, h, qpos)]);
+#pragma unroll
+            for (int c = 0; c < D; ++c) {
+                ak[c] = fmaf(ds, qp[c], ak[c]);
+                av[c] = fmaf(pr, gp[c], av[c]);
+            }
+        }
+    }
+    float *dk = static_cast<float *>(p.dk) + (kpos * p.Hkv + kvh) * D;
+    float *dv = static_cast<float *>(p.dv) + (kpos * p.Hkv + kvh) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        dk[c] = p.scale * ak[c];
+        dv[c] = av[c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 kernels on v_mfma_f32_32x32x16_bf16 (operand layouts as in the forward:
+// lane l supplies row l % 32 of A / column l % 32 of B with k-slots
+// 8*(l/32) .. +7; register r of the accumulator holds C[8*(r/4) + 4*(l/32) +
+// r%4][l % 32]).  LDS tiles are row-major with a 16-byte pad per row.  A
+// transposed operand (a 32-row block of a tile read down its columns) comes
+// from two ds_read_b64_tr_b16: within a 16-lane group that instruction gives
+// lane i element e of the 8 bytes read by lane 4e + i/4, so lane j of the
+// group addresses row r0 + j/4, columns c0 + 4*(j%4); the result holds
+// column c0 + (lane % 16) of rows r0 .. r0+3.
+
+template <int D>
+__device__ __forceinline__ bf16x8 read_rows_tr(const char *tile, int row0, int col0, int hi, int l16, int g2) {
+    constexpr int PITCH = 2 * D + 16;
+    s16x4 h2[2];
+#pragma unroll
+    for (int jh = 0; jh < 2; ++jh) {
+        const int row = row0 + 8 * jh + 4 * hi + (l16 >> 2);
+        const int col = col0 + 16 * g2 + 4 * (l16 & 3);
+        h2[jh] = lds_read_tr16(tile + row * PITCH + col * 2);
+    }
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Copy `rows` rows of D bf16 (global row stride `rstride` elements, first row
+// `base`) into a padded LDS tile; rows at or past `nvalid` are zero.
+template <int D>
+__device__ __forceinline__ void stage_rows(char *tile, const bf16 *base, int64_t rstride, int rows, int nvalid) {
+    constexpr int CH = D / 8, PITCH = 2 * D + 16;
+    for (int c = threadIdx.x; c < rows * CH; c += blockDim.x) {
+        const int r = c / CH, cc = c - r * CH;
+        uint4 x = {0, 0, 0, 0};
+        if (r < nvalid) x = *reinterpret_cast<const uint4 *>(base + r * rstride + cc * 8);
+        *reinterpret_cast<uint4 *>(tile + r * PITCH + cc * 16) = x;
+    }
+}
+
+// Store a [D dims x 32] accumulator block set (lane = row l % 32 of the
+// output, registers = dims) as bf16, times `mul`.
+template <int D>
+__device__ __forceinline__ void store_rows(bf16 *out, const f32x16 (&acc)[D / 32], float mul, int hi) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            bf16x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = (bf16)(acc[db][4 * r4 + e] * mul);
+            *reinterpret_cast<bf16x4 *>(out + db * 32 + 8 * r4 + 4 * hi) = y;
+        }
+}
+
+// 2. dK, dV.  Workgroup = 4 waves x 32 keys of one (b, kv head, sub); per
+// query tile (32 queries of one head of the group):
+//   S = Q K^T, dP = dO V^T      [32 q x 32 k]: lane = key, registers = queries
+//   P = exp(S*scale - lse), dS = P (dP - D)
+//   dV^T += dO^T P, dK^T += Q^T dS   [D x 32 k]
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nkblk) {
+    constexpr int PITCH = 2 * D + 16;
+    __shared__ __attribute__((aligned(16))) char Qs[BQT * PITCH];
+    __shared__ __attribute__((aligned(16))) char Gs[BQT * PITCH];
+    __shared__ __attribute__((aligned(16))) float Ls[BQT], Ds[BQT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int g = p.Hq / p.Hkv;
+
+    // workgroup -> (key block, b, kv head, sub); low key blocks (most queries) first
+    const int kblk = (int)(blockIdx.x % nkblk);
+    int rest = (int)(blockIdx.x / nkblk);
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+    const int j0 = kblk * BKW;
+    const int jw0 = j0 + 32 * wave;  // this wave's first key
+    const int myk = jw0 + l32;
+    const bool kvalid = myk < p.Lsub;
+
+    const int64_t qrs = (int64_t)p.Hq * D, krs = (int64_t)p.Hkv * D;
+    const int64_t kpos = sub_pos(p, b, sub, kvalid ? myk : 0);
+    // B operands K^T and V^T: lane = key, k-slots = dims 16*ks + 8*hi .. +7
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const bf16 *kr = static_cast<const bf16 *>(p.k) + kpos * krs + (int64_t)kvh * D + 8 * hi;
+        const bf16 *vr = static_cast<const bf16 *>(p.v) + kpos * krs + (int64_t)kvh * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            kf[ks] = kvalid ? *reinterpret_cast<const bf16x8 *>(kr + 16 * ks) : bf16x8{};
+            vf[ks] = kvalid ? *reinterpret_cast<const bf16x8 *>(vr + 16 * ks) : bf16x8{};
+        }
+    }
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
+
+    const float c2 = p.scale * kLog2e;
+    // queries that see keys [j0, j0 + 128): i >= j0 and i - j < weff
+    const int iend = p.weff ? min(p.Lsub, j0 + BKW - 1 + p.weff) : p.Lsub;
+    for (int hh = 0; hh < g; ++hh) {
+        const int h = kvh * g + hh;
+        for (int i0 = j0; i0 < iend; i0 += BQT) {
+            __syncthreads();  // previous tile consumed
+            const int nvalid = min(BQT, p.Lsub - i0);
+            const int64_t qpos0 = sub_pos(p, b, sub, i0);
+            stage_rows<D>(Qs, static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D, p.stride * qrs, BQT,
+                          nvalid);
+            stage_rows<D>(Gs, static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D, p.stride * qrs, BQT,
+                          nvalid);
+            if (tid < BQT) {
+                const int64_t st = row_stat(p, b, h, qpos0 + (int64_t)tid * p.stride);
+                Ls[tid] = tid < nvalid ? p.lse[st] * kLog2e : 0.f;
+                Ds[tid] = tid < nvalid ? p.drow[st] : 0.f;
+            }
+            __syncthreads();
+
+            const bool active = (i0 + BQT - 1 >= jw0) && (p.weff == 0 || i0 < jw0 + 31 + p.weff) && jw0 < p.Lsub;
+            if (!active) continue;
+            const bool need_mask = (i0 < jw0 + 31) || (i0 + BQT > p.Lsub) || (jw0 + 32 > p.Lsub) ||
+                                   (p.weff != 0 && i0 + BQT - 1 - jw0 >= p.weff);
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(Qs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
+                const bf16x8 ga = *reinterpret_cast<const bf16x8 *>(Gs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
+                s = mfma32(qa, kf[ks], s);
+                dp = mfma32(ga, vf[ks], dp);
+            }
+            // register r = 8*m2 + jj holds query 16*m2 + 8*(jj/4) + 4*hi + jj%4
+            bf16x8 pop[2], dsop[2];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int r = 8 * m2 + jj;
+                    const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
+                    const int i = i0 + qi;
+                    bool vis = true;
+                    if (need_mask)
+                        vis = kvalid && i < p.Lsub && i >= myk && (p.weff == 0 || i - myk < p.weff);
+                    const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -Ls[qi])) : 0.f;
+                    pop[m2][jj] = (bf16)pr;
+                    dsop[m2][jj] = (bf16)(pr * (dp[r] - Ds[qi]));
+                }
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    dv[db] = mfma32(read_rows_tr<D>(Gs, 16 * m2, 32 * db, hi, l16, g2), pop[m2], dv[db]);
+                    dk[db] = mfma32(read_rows_tr<D>(Qs, 16 * m2, 32 * db, hi, l16, g2), dsop[m2], dk[db]);
+                }
+        }
+    }
+    if (kvalid) {
+        const int64_t off = kpos * krs + (int64_t)kvh * D;
+        store_rows<D>(static_cast<bf16 *>(p.dk) + off, dk, p.scale, hi);
+        store_rows<D>(static_cast<bf16 *>(p.dv) + off, dv, 1.f, hi);
+    }
+}
+
+// 3. dQ.  Workgroup = 4 waves = HG heads of one GQA group x TB blocks of 32
+// queries (HG*TB = 4), sharing 64-key K/V tiles; per tile:
+//   S^T = K Q^T, dP^T = V dO^T   [64 k x 32 q]: lane = query, registers = keys
+//   dS^T = P^T (dP^T - D);  dQ^T += K^T dS^T   [D x 32 q]
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, int TB, int nqblk) {
+    constexpr int PITCH = 2 * D + 16;
+    __shared__ __attribute__((aligned(16))) char Ks[BKT * PITCH];
+    __shared__ __attribute__((aligned(16))) char Vs[BKT * PITCH];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int g = p.Hq / p.Hkv, ngrp = g / HG;
+
+    // workgroup -> (q block, b, kv head, head group, sub); longest blocks first
+    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
+    const int qblk = nqblk - 1 - (int)(blockIdx.x / nrest);
+    int rest = (int)(blockIdx.x % nrest);
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int hgrp = rest % ngrp; rest /= ngrp;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+
+    const int q0 = qblk * 32 * TB;
+    const int h = kvh * g + hgrp * HG + wave % HG;
+    const int qw0 = q0 + 32 * (wave / HG);
+    const int myq = qw0 + l32;
+    const bool qvalid = myq < p.Lsub;
+    const int64_t qrs = (int64_t)p.Hq * D, krs = (int64_t)p.Hkv * D;
+    const int64_t pos = sub_pos(p, b, sub, qvalid ? myq : 0);
+
+    // B operands Q^T and dO^T: lane = query, k-slots = dims 16*ks + 8*hi .. +7
+    bf16x8 qf[D / 16], gf[D / 16];
+    {
+        const bf16 *qr = static_cast<const bf16 *>(p.q) + pos * qrs + (int64_t)h * D + 8 * hi;
+        const bf16 *gr = static_cast<const bf16 *>(p.dout) + pos * qrs + (int64_t)h * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            qf[ks] = qvalid ? *reinterpret_cast<const bf16x8 *>(qr + 16 * ks) : bf16x8{};
+            gf[ks] = qvalid ? *reinterpret_cast<const bf16x8 *>(gr + 16 * ks) : bf16x8{};
+        }
+    }
+    const float c2 = p.scale * kLog2e;
+    const float lse2 = qvalid ? p.lse[row_stat(p, b, h, pos)] * kLog2e : 0.f;
+    const float Dq = qvalid ? p.drow[row_stat(p, b, h, pos)] : 0.f;
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+    const int kend = min(q0 + 32 * TB, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    for (int t0 = kbeg & ~(BKT - 1); t0 < kend; t0 += BKT) {
+        __syncthreads();  // previous tile consumed
+        const int nvalid = min(BKT, p.Lsub - t0);
+        const int64_t kpos0 = sub_pos(p, b, sub, t0);
+        stage_rows<D>(Ks, static_cast<const bf16 *>(p.k) + kpos0 * krs + (int64_t)kvh * D, p.stride * krs, BKT,
+                      nvalid);
+        stage_rows<D>(Vs, static_cast<const bf16 *>(p.v) + kpos0 * krs + (int64_t)kvh * D, p.stride * krs, BKT,
+                      nvalid);
+        __syncthreads();
+
+        const bool active = (t0 <= qw0 + 31) && (p.weff == 0 || t0 + BKT - 1 > qw0 - p.weff);
+        if (!active) continue;
+        const bool need_mask =
+            (t0 + BKT - 1 > qw0) || (t0 + BKT > p.Lsub) || (p.weff != 0 && t0 <= qw0 + 31 - p.weff);
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const int off = (kb * 32 + l32) * PITCH + (16 * ks + 8 * hi) * 2;
+                s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + off), qf[ks], s[kb]);
+                dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(Vs + off), gf[ks], dp[kb]);
+            }
+        }
+        // register r of block kb holds key t0 + 32*kb + 8*(r/4) + 4*hi + r%4
+        bf16x8 dsop[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int r = 8 * m2 + jj;
+                    const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                    bool vis = true;
+                    if (need_mask) vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                    const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2)) : 0.f;
+                    dsop[kb * 2 + m2][jj] = (bf16)(pr * (dp[kb][r] - Dq));
+                }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    dq[db] = mfma32(read_rows_tr<D>(Ks, 32 * kb + 16 * m2, 32 * db, hi, l16, g2), dsop[kb * 2 + m2],
+                                    dq[db]);
+    }
+    if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + pos * qrs + (int64_t)h * D, dq, p.scale, hi);
+}
+
+template <typename T>
+hipError_t launch_drow(const BwdArgs &a, hipStream_t st) {
+    const int64_t rows = (int64_t)a.B * a.nL * a.Hq;
+    const int64_t grid = (rows + 15) / 16;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    switch (a.d) {
+        case 32: hipLaunchKernelGGL((bwd_drow_kernel<T, 32>), dim3((unsigned)grid), dim3(256), 0, st, a); break;
+        case 64: hipLaunchKernelGGL((bwd_drow_kernel<T, 64>), dim3((unsigned)grid), dim3(256), 0, st, a); break;
+        case 128: hipLaunchKernelGGL((bwd_drow_kernel<T, 128>), dim3((unsigned)grid), dim3(256), 0, st, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
+    const int g = a.Hq / a.Hkv;
+    const int nkblk = (a.Lsub + BKW - 1) / BKW;
+    const int64_t kgrid = (int64_t)nkblk * a.B * a.Hkv * a.nsub;
+    const int HG = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
+    const int TB = 4 / HG;
+    const int nqblk = (a.Lsub + 32 * TB - 1) / (32 * TB);
+    const int64_t qgrid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
+    if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3((unsigned)kgrid), dim3(256), 0, st, a, nkblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3((unsigned)qgrid), dim3(256), 0, st, a, HG, TB, nqblk);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32_d(const BwdArgs &a, hipStream_t st) {
+    const int64_t qrows = (int64_t)a.B * a.nsub * a.Lsub * a.Hq;
+    const int64_t krows = (int64_t)a.B * a.nsub * a.Lsub * a.Hkv;
+    if ((qrows + 63) / 64 > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3((unsigned)((qrows + 63) / 64)), dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel<D>, dim3((unsigned)((krows + 63) / 64)), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int nL, int Hq) { return (size_t)B * Hq * nL * sizeof(float); }
+
+hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st) {
+    hipError_t e = launch_drow<bf16>(a, st);
+    if (e != hipSuccess) return e;
+    switch (a.d) {
+        case 32: return launch_bf16_d<32>(a, st);
+        case 64: return launch_bf16_d<64>(a, st);
+        case 128: return launch_bf16_d<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st) {
+    hipError_t e = launch_drow<float>(a, st);
+    if (e != hipSuccess) return e;
+    switch (a.d) {
+        case 32: return launch_f32_d<32>(a, st);
+        case 64: return launch_f32_d<64>(a, st);
+        case 128: return launch_f32_d<128>(a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hd

@@ -32,7 +32,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "hd_expand_embed", "hd_sfa_fwd", "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
+        "hd_expand_embed", "hd_sfa_fwd", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
         "hd_status_string", "hd_last_error", "hd_version"])
 
 
@@ -102,6 +103,34 @@ def test_workspace_size_is_monotone_and_zero_on_bad_sizes(lib):
     assert 0 < a <= b
     # partials: B*n*Hq*(d+2) floats per split
     assert a % (64 * 4 * 32 * 130 * 4) == 0
+
+
+def bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
+             B=1, L=8, n=2, Hq=4, Hkv=2, d=64, mode=0, window=0, scale=0.0, dt=0,
+             workspace=FAKE, workspace_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.hd_sfa_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), hd.HD_ERR_INVALID), (dict(L=0), hd.HD_ERR_INVALID), (dict(Hq=3), hd.HD_ERR_INVALID),
+    (dict(window=-1), hd.HD_ERR_INVALID), (dict(dout=None), hd.HD_ERR_INVALID),
+    (dict(lse=None), hd.HD_ERR_INVALID), (dict(lse=FAKE + 4), hd.HD_ERR_INVALID),
+    (dict(dk=FAKE + 8), hd.HD_ERR_INVALID), (dict(workspace=None), hd.HD_ERR_INVALID),
+    (dict(workspace_bytes=1 * 4 * 16 * 4 - 1), hd.HD_ERR_INVALID),   # B*Hq*nL*4 = 256 bytes needed
+    (dict(d=96), hd.HD_ERR_UNSUPPORTED), (dict(dt=3), hd.HD_ERR_UNSUPPORTED), (dict(mode=5), hd.HD_ERR_UNSUPPORTED),
+])
+def test_bwd_validation(lib, kw, code):
+    assert bwd(lib, **kw) == code
+    assert hd.last_error() != ""
+
+
+def test_bwd_workspace_size(lib):
+    f = hd.hd_sfa_bwd_workspace_bytes
+    assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4
+    assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4
+    assert f(0, 8, 2, 4, 2, 64) == 0 and f(1, 8, 2, 4, 3, 64) == 0 and f(1, 8, 2, 4, 2, 96) == 0
 
 
 def test_embed_validation(lib):
