@@ -18,9 +18,10 @@
 // Three launches, no atomics, every output element written once:
 //   1. D_i = dO_i . O_i for every query row (fp32, into the workspace);
 //   2. dK, dV: a workgroup owns 128 keys of one (batch, kv head, sub-sequence)
-//      and walks the query tiles (all heads of the group) that see them;
+//      and walks the query tiles (all heads of the group) that see them,
+//      staging the tiles of up to four heads per barrier;
 //   3. dQ: a wave owns 32 queries of one head and walks the key tiles they see
-//      (the forward's loop, recomputing P from lse).
+//      (the forward's loop, recomputing P from lse), 128 keys per barrier.
 #include "attn_common.h"
 
 namespace hd {
@@ -180,14 +181,20 @@ __device__ __forceinline__ bf16x8 read_rows_tr(const char *tile, int row0, int c
 
 // Copy `rows` rows of D bf16 (global row stride `rstride` elements, first row
 // `base`) into a padded LDS tile; rows at or past `nvalid` are zero.
-template <int D>
-__device__ __forceinline__ void stage_rows(char *tile, const bf16 *base, int64_t rstride, int rows, int nvalid) {
-    constexpr int CH = D / 8, PITCH = 2 * D + 16;
-    for (int c = threadIdx.x; c < rows * CH; c += blockDim.x) {
-        const int r = c / CH, cc = c - r * CH;
-        uint4 x = {0, 0, 0, 0};
-        if (r < nvalid) x = *reinterpret_cast<const uint4 *>(base + r * rstride + cc * 8);
-        *reinterpret_cast<uint4 *>(tile + r * PITCH + cc * 16) = x;
+template <int D, int ROWS>
+__device__ __forceinline__ void stage_rows(char *tile, const bf16 *base, int64_t rstride, int nvalid) {
+    constexpr int CH = D / 8, PITCH = 2 * D + 16, PER = (ROWS * CH + 255) / 256;
+    uint4 x[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {  // all loads first, then all stores
+        const int c = threadIdx.x + 256 * u, r = c / CH, cc = c - r * CH;
+        x[u] = uint4{0, 0, 0, 0};
+        if (c < ROWS * CH && r < nvalid) x[u] = *reinterpret_cast<const uint4 *>(base + r * rstride + cc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int c = threadIdx.x + 256 * u, r = c / CH, cc = c - r * CH;
+        if (c < ROWS * CH) *reinterpret_cast<uint4 *>(tile + r * PITCH + cc * 16) = x[u];
     }
 }
 
@@ -214,18 +221,21 @@ __device__ __forceinline__ void store_rows(bf16 *out, const f32x16 (&acc)[D / 32
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nkblk) {
     constexpr int PITCH = 2 * D + 16;
-    __shared__ __attribute__((aligned(16))) char Qs[BQT * PITCH];
-    __shared__ __attribute__((aligned(16))) char Gs[BQT * PITCH];
-    __shared__ __attribute__((aligned(16))) float Ls[BQT], Ds[BQT];
+    constexpr int HS = 4;  // heads of the group staged per round
+    __shared__ __attribute__((aligned(16))) char Qs[HS][BQT * PITCH];
+    __shared__ __attribute__((aligned(16))) char Gs[HS][BQT * PITCH];
+    __shared__ __attribute__((aligned(16))) float Ls[HS][BQT], Ds[HS][BQT];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
     const int g = p.Hq / p.Hkv;
 
-    // workgroup -> (key block, b, kv head, sub); low key blocks (most queries) first
-    const int kblk = (int)(blockIdx.x % nkblk);
-    int rest = (int)(blockIdx.x / nkblk);
+    // workgroup -> (key block, b, kv head, sub); the low key blocks of every
+    // group (they see the most queries) are dispatched first
+    const int ngroups = p.B * p.Hkv * p.nsub;
+    const int kblk = (int)(blockIdx.x / ngroups);
+    int rest = (int)(blockIdx.x % ngroups);
     const int sub = rest % p.nsub; rest /= p.nsub;
     const int kvh = rest % p.Hkv;
     const int b = rest / p.Hkv;
@@ -254,20 +264,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
     const float c2 = p.scale * kLog2e;
     // queries that see keys [j0, j0 + 128): i >= j0 and i - j < weff
     const int iend = p.weff ? min(p.Lsub, j0 + BKW - 1 + p.weff) : p.Lsub;
-    for (int hh = 0; hh < g; ++hh) {
-        const int h = kvh * g + hh;
+    for (int h0 = 0; h0 < g; h0 += HS) {
+        const int nh = min(HS, g - h0);
         for (int i0 = j0; i0 < iend; i0 += BQT) {
-            __syncthreads();  // previous tile consumed
+            __syncthreads();  // previous tiles consumed
             const int nvalid = min(BQT, p.Lsub - i0);
             const int64_t qpos0 = sub_pos(p, b, sub, i0);
-            stage_rows<D>(Qs, static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D, p.stride * qrs, BQT,
-                          nvalid);
-            stage_rows<D>(Gs, static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D, p.stride * qrs, BQT,
-                          nvalid);
-            if (tid < BQT) {
-                const int64_t st = row_stat(p, b, h, qpos0 + (int64_t)tid * p.stride);
-                Ls[tid] = tid < nvalid ? p.lse[st] * kLog2e : 0.f;
-                Ds[tid] = tid < nvalid ? p.drow[st] : 0.f;
+            for (int hh = 0; hh < nh; ++hh) {
+                const int h = kvh * g + h0 + hh;
+                stage_rows<D, BQT>(Qs[hh], static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D,
+                                   p.stride * qrs, nvalid);
+                stage_rows<D, BQT>(Gs[hh], static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D,
+                                   p.stride * qrs, nvalid);
+            }
+            if (tid < BQT * nh) {
+                const int hh = tid / BQT, r = tid % BQT;
+                const int64_t st = row_stat(p, b, kvh * g + h0 + hh, qpos0 + (int64_t)r * p.stride);
+                Ls[hh][r] = r < nvalid ? p.lse[st] * kLog2e : 0.f;
+                Ds[hh][r] = r < nvalid ? p.drow[st] : 0.f;
             }
             __syncthreads();
 
@@ -275,37 +289,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
             if (!active) continue;
             const bool need_mask = (i0 < jw0 + 31) || (i0 + BQT > p.Lsub) || (jw0 + 32 > p.Lsub) ||
                                    (p.weff != 0 && i0 + BQT - 1 - jw0 >= p.weff);
-            f32x16 s = f32x16{}, dp = f32x16{};
+            for (int hh = 0; hh < nh; ++hh) {
+                const char *qs = Qs[hh], *gs = Gs[hh];
+                f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(Qs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
-                const bf16x8 ga = *reinterpret_cast<const bf16x8 *>(Gs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
-                s = mfma32(qa, kf[ks], s);
-                dp = mfma32(ga, vf[ks], dp);
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const bf16x8 qa = *reinterpret_cast<const bf16x8 *>(qs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
+                    const bf16x8 ga = *reinterpret_cast<const bf16x8 *>(gs + l32 * PITCH + (16 * ks + 8 * hi) * 2);
+                    s = mfma32(qa, kf[ks], s);
+                    dp = mfma32(ga, vf[ks], dp);
+                }
+                // register r = 8*m2 + jj holds query 16*m2 + 8*(jj/4) + 4*hi + jj%4
+                bf16x8 pop[2], dsop[2];
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int r = 8 * m2 + jj;
+                        const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
+                        const int i = i0 + qi;
+                        bool vis = true;
+                        if (need_mask)
+                            vis = kvalid && i < p.Lsub && i >= myk && (p.weff == 0 || i - myk < p.weff);
+                        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -Ls[hh][qi]));
+                        const float pr = vis ? e : 0.f;  // a select, not a branch
+                        pop[m2][jj] = (bf16)pr;
+                        dsop[m2][jj] = (bf16)(pr * (dp[r] - Ds[hh][qi]));
+                    }
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        dv[db] = mfma32(read_rows_tr<D>(gs, 16 * m2, 32 * db, hi, l16, g2), pop[m2], dv[db]);
+                        dk[db] = mfma32(read_rows_tr<D>(qs, 16 * m2, 32 * db, hi, l16, g2), dsop[m2], dk[db]);
+                    }
             }
-            // register r = 8*m2 + jj holds query 16*m2 + 8*(jj/4) + 4*hi + jj%4
-            bf16x8 pop[2], dsop[2];
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int r = 8 * m2 + jj;
-                    const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
-                    const int i = i0 + qi;
-                    bool vis = true;
-                    if (need_mask)
-                        vis = kvalid && i < p.Lsub && i >= myk && (p.weff == 0 || i - myk < p.weff);
-                    const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c2, -Ls[qi])) : 0.f;
-                    pop[m2][jj] = (bf16)pr;
-                    dsop[m2][jj] = (bf16)(pr * (dp[r] - Ds[qi]));
-                }
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    dv[db] = mfma32(read_rows_tr<D>(Gs, 16 * m2, 32 * db, hi, l16, g2), pop[m2], dv[db]);
-                    dk[db] = mfma32(read_rows_tr<D>(Qs, 16 * m2, 32 * db, hi, l16, g2), dsop[m2], dk[db]);
-                }
         }
     }
     if (kvalid) {
@@ -322,8 +340,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, int TB, int nqblk) {
     constexpr int PITCH = 2 * D + 16;
-    __shared__ __attribute__((aligned(16))) char Ks[BKT * PITCH];
-    __shared__ __attribute__((aligned(16))) char Vs[BKT * PITCH];
+    __shared__ __attribute__((aligned(16))) char Ks[2][BKT * PITCH];  // two 64-key sub-tiles per round
+    __shared__ __attribute__((aligned(16))) char Vs[2][BKT * PITCH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,54 +385,62 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
 
     const int kend = min(q0 + 32 * TB, p.Lsub);
     const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
-    for (int t0 = kbeg & ~(BKT - 1); t0 < kend; t0 += BKT) {
-        __syncthreads();  // previous tile consumed
-        const int nvalid = min(BKT, p.Lsub - t0);
-        const int64_t kpos0 = sub_pos(p, b, sub, t0);
-        stage_rows<D>(Ks, static_cast<const bf16 *>(p.k) + kpos0 * krs + (int64_t)kvh * D, p.stride * krs, BKT,
-                      nvalid);
-        stage_rows<D>(Vs, static_cast<const bf16 *>(p.v) + kpos0 * krs + (int64_t)kvh * D, p.stride * krs, BKT,
-                      nvalid);
-        __syncthreads();
-
-        const bool active = (t0 <= qw0 + 31) && (p.weff == 0 || t0 + BKT - 1 > qw0 - p.weff);
-        if (!active) continue;
-        const bool need_mask =
-            (t0 + BKT - 1 > qw0) || (t0 + BKT > p.Lsub) || (p.weff != 0 && t0 <= qw0 + 31 - p.weff);
-        f32x16 s[2], dp[2];
+    for (int tr = kbeg & ~(BKT - 1); tr < kend; tr += 2 * BKT) {
+        __syncthreads();  // previous tiles consumed
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = dp[kb] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
-                const int off = (kb * 32 + l32) * PITCH + (16 * ks + 8 * hi) * 2;
-                s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(Ks + off), qf[ks], s[kb]);
-                dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(Vs + off), gf[ks], dp[kb]);
-            }
+        for (int u = 0; u < 2; ++u) {
+            const int t0 = tr + u * BKT;
+            const int nvalid = max(0, min(BKT, min(p.Lsub, kend) - t0));
+            const int64_t kpos0 = sub_pos(p, b, sub, nvalid ? t0 : 0);
+            stage_rows<D, BKT>(Ks[u], static_cast<const bf16 *>(p.k) + kpos0 * krs + (int64_t)kvh * D,
+                               p.stride * krs, nvalid);
+            stage_rows<D, BKT>(Vs[u], static_cast<const bf16 *>(p.v) + kpos0 * krs + (int64_t)kvh * D,
+                               p.stride * krs, nvalid);
         }
-        // register r of block kb holds key t0 + 32*kb + 8*(r/4) + 4*hi + r%4
-        bf16x8 dsop[4];
+        __syncthreads();
+        for (int u = 0; u < 2; ++u) {
+            const int t0 = tr + u * BKT;
+            const char *ks_ = Ks[u], *vs_ = Vs[u];
+            const bool active = (t0 < kend) && (t0 <= qw0 + 31) && (p.weff == 0 || t0 + BKT - 1 > qw0 - p.weff);
+            if (!active) continue;
+            const bool need_mask =
+                (t0 + BKT - 1 > qw0) || (t0 + BKT > p.Lsub) || (p.weff != 0 && t0 <= qw0 + 31 - p.weff);
+            f32x16 s[2], dp[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb) {
+                s[kb] = dp[kb] = f32x16{};
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2)
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int r = 8 * m2 + jj;
-                    const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    bool vis = true;
-                    if (need_mask) vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
-                    const float pr = vis ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2)) : 0.f;
-                    dsop[kb * 2 + m2][jj] = (bf16)(pr * (dp[kb][r] - Dq));
+                for (int ks = 0; ks < D / 16; ++ks) {
+                    const int off = (kb * 32 + l32) * PITCH + (16 * ks + 8 * hi) * 2;
+                    s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(ks_ + off), qf[ks], s[kb]);
+                    dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(vs_ + off), gf[ks], dp[kb]);
                 }
+            }
+            // register r of block kb holds key t0 + 32*kb + 8*(r/4) + 4*hi + r%4
+            bf16x8 dsop[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2)
+                for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db)
-                    dq[db] = mfma32(read_rows_tr<D>(Ks, 32 * kb + 16 * m2, 32 * db, hi, l16, g2), dsop[kb * 2 + m2],
-                                    dq[db]);
+                    for (int jj = 0; jj < 8; ++jj) {
+                        const int r = 8 * m2 + jj;
+                        const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
+                        bool vis = true;
+                        if (need_mask) vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                        const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2));
+                        const float pr = vis ? e : 0.f;  // a select, not a branch
+                        dsop[kb * 2 + m2][jj] = (bf16)(pr * (dp[kb][r] - Dq));
+                    }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        dq[db] = mfma32(read_rows_tr<D>(ks_, 32 * kb + 16 * m2, 32 * db, hi, l16, g2),
+                                        dsop[kb * 2 + m2], dq[db]);
+        }
     }
     if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + pos * qrs + (int64_t)h * D, dq, p.scale, hi);
 }
