@@ -6,6 +6,7 @@ are already resident in HBM:
   intra prefill  n=4, L=4096 (nL=16384), 32 q / 8 kv heads, d=128, bf16   <- headline
   intra prefill  n=1, L=4096 control (for the n=4 / n=1 time ratio)
   cross prefill  same shapes as the headline, dense causal over 16384 positions
+  backward       dQ, dK, dV of the headline intra-stream layer (given o, lse, dO)
   decode         64 sequences, 8192 cached tokens x 4 streams, 32 q / 8 kv heads,
                  intra and cross (one new token, 4 stream queries each)
 With --long, also the 32k-token layers (n=4, nL=131072, 16 q / 4 kv heads):
@@ -168,6 +169,26 @@ def main():
         comps["intra_n1"] = prefill(I1)
     if want("cross_n4"):
         comps["cross_n4"] = prefill(X)
+    def backward(cfg):
+        """(callable, useful flops, algorithmic bytes) of one backward call of
+        the layer; o and lse come from one forward call outside the timed
+        region, dO is a seeded draw like q, k, v."""
+        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+        dout = synth.normal(q.shape, 9, cfg.dtype, dev)
+        o, lse = hd.sfa_fwd(q, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(hd.hd_sfa_bwd_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
+                         dtype=torch.uint8, device=dev)
+        # useful FLOPs: five products of the forward's size over the visible
+        # pairs (S recomputed, dP, dV, dK, dQ) = 2.5x the forward's count
+        fl = 2.5 * useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+        # q, o, dO, k, v read; dq, dk, dv written; lse read, D written and read
+        by = 2 * (4 * q.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.n * cfg.L
+        return (lambda: hd.hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, cfg.n, cfg.mode, cfg.window,
+                                      workspace=ws), fl, by)
+
+    if want("bwd_intra_n4"):
+        comps["bwd_intra_n4"] = backward(I)
     if want("decode_intra") or want("decode_cross"):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)
