@@ -25,6 +25,13 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, unsigned lds_base) {
                  : "memory", "m0");
 }
 
+// Same copy from a wave-uniform base (scalar registers) plus a 32-bit per-lane
+// byte offset (no 64-bit address arithmetic per lane).
+__device__ __forceinline__ void lds_dma16_s(const void *base, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ unsigned lds_addr(const char *p) {
     return (unsigned)(size_t)((__attribute__((address_space(3))) const char *)p);
 }

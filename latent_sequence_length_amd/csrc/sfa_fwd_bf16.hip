@@ -219,6 +219,10 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //   * K and V tiles are fetched with direct-to-LDS 16-byte loads
 //     (global_load_lds), double-buffered: tile t+1 is in flight while tile t
 //     is computed, with no VGRPs spent on staging and one barrier per tile;
+//     the tile base is a scalar and each lane's offset is fixed, so issuing a
+//     copy costs no vector ALU work;
+//   * the QK^T MFMAs run as two interleaved accumulator chains with the K
+//     operand reads scheduled eight ahead;
 //   * LDS rows are 256 B with the 16-byte chunk index XOR-swizzled by the row
 //     (sw(r) = 2*(r%8) + (r/8)%2), so the K-operand reads (16 rows, one chunk)
 //     and the transposed V reads (8 rows, four chunks) are bank-conflict free;
@@ -232,6 +236,10 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
 //     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
 constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
+
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
 
 // One tile of the d=128 loop: wait for tile `it` (in buffer `cur`), start
 // the DMA of tile it+1 into `nxt`, then compute tile `it`.  `cur` and `nxt`
@@ -261,18 +269,26 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
 
     f32x16 sacc[2];
     __builtin_amdgcn_s_setprio(1);  // the wave issuing MFMAs wins arbitration on its SIMD
+    // two independent 32-key accumulator chains, interleaved; the K-operand
+    // reads are scheduled eight ahead of the MFMAs that consume them
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = f32x16{};
-        const int r = kb * 32 + l32;
-        const char *row = kbuf + r * 256;
-        const int sw = swz128(r);
+    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x16{};
+    const int ksw = swz128(l32) ^ hi;  // swz128(32*kb + l32) == swz128(l32); 2*ks + hi == (2*ks) ^ hi
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(row + (((2 * ks + hi) ^ sw) << 4));
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + (kb * 32 + l32) * 256 + (((2 * ks) ^ ksw) << 4));
             sacc[kb] = mfma32(a, qop[ks], sacc[kb]);
         }
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
 
     __builtin_amdgcn_s_setprio(0);
     float mx = -INFINITY;
@@ -290,10 +306,15 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
                 sacc[kb][r] = (u <= span) ? sacc[kb][r] : -INFINITY;
             }
     }
+    {
+        float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sacc[kb][r], sacc[kb][r + 1]));
+        for (int r = 2; r < 16; r += 2) {  // two chains of three-input max
+            m0 = fmaxf(m0, fmaxf(sacc[0][r], sacc[0][r + 1]));
+            m1 = fmaxf(m1, fmaxf(sacc[1][r], sacc[1][r + 1]));
+        }
+        mx = fmaxf(m0, m1);
+    }
     mx = pair_max(mx);
     const float m_tile = mx * scale_log2;
     const float m_new = (m_tile > st.m_run + 8.f) ? m_tile : st.m_run;
@@ -393,16 +414,25 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
         lrow[i] = (wave * PER + i) * 4 + (lane >> 4);
         lchunk[i] = ((lane & 15) ^ swz128(lrow[i])) * 8;
     }
+    unsigned boff[PER];  // per-lane byte offsets within a tile (rows unclamped)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) boff[i] = (unsigned)(lrow[i] * rstride + lchunk[i]) * 2u;
     auto issue = [&](int t0, char *dst) {
         const int64_t tbase = (bpos + (int64_t)t0 * p.stride) * krs;
         const bf16 *kt = kg + tbase, *vt = vg + tbase;
         const int rmax = p.Lsub - 1 - t0;
+        unsigned bo[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) bo[i] = boff[i];
+        if (rmax < KT - 1) {  // tail tile: rows past the end re-read the last row
+#pragma unroll
+            for (int i = 0; i < PER; ++i) bo[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunk[i]) * 2u;
+        }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
-            const int off = min(lrow[i], rmax) * rstride + lchunk[i];
             const int s0 = (wave * PER + i) * 64;
-            lds_dma16(kt + off, lds_addr(dst + s0 * 16));
-            lds_dma16(vt + off, lds_addr(dst + TILE + s0 * 16));
+            lds_dma16_s(kt, bo[i], lds_addr(dst + s0 * 16));
+            lds_dma16_s(vt, bo[i], lds_addr(dst + TILE + s0 * 16));
         }
     };
     if (ntiles > 0) issue(tfirst, buf0);
