@@ -354,3 +354,40 @@ int oracle_sfa_bwd_rows(const void *q, const void *k, const void *v, const void 
     }
     return bad ? -1 : 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Rotary position embedding at the expanded positions.  "Hidden Decoding at
+ * Scale", "Multi-Stream Expansion and Training Objective": the expanded
+ * sequence S_1 .. S_nL is fed to the Transformer with contiguous RoPE
+ * positions, so the position of S_t is t (the expanded index), not the token
+ * index i(t).  The pages do not restate RoPE itself; the reading taken is the
+ * common "rotate half" form: with h = d/2 and frequency
+ * f_c = theta^(-2c/d) for c in [0, h),
+ *   out[c]     = x[c]     cos(t f_c) - x[c + h] sin(t f_c)
+ *   out[c + h] = x[c + h] cos(t f_c) + x[c]     sin(t f_c)
+ * x [B][T][H][d] (float32 or bf16 bits); out [B][T][H][d] double.  The
+ * position of row (b, t) is t + pos_mul * pos_base[b] (pos_base may be NULL):
+ * a prefill passes NULL; a decode step passes the cached token counts with
+ * pos_mul = n, so stream s of the new token sits at len*n + s.
+ * Returns 0 or -1.
+ * ------------------------------------------------------------------------- */
+int oracle_rope(const void *x, int dtype, int B, int T, int H, int d, const int32_t *pos_base,
+                int64_t pos_mul, double theta, double *out) {
+    if (B < 1 || T < 1 || H < 1 || d < 2 || d % 2 || theta <= 0.0 || pos_mul < 0) return -1;
+    const int h = d / 2;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < T; ++t) {
+            const double pos = (double)t + (pos_base ? (double)pos_mul * (double)pos_base[b] : 0.0);
+            for (int64_t hh = 0; hh < H; ++hh) {
+                const int64_t row = ((b * T + t) * H + hh) * d;
+                for (int c = 0; c < h; ++c) {
+                    const double f = pow(theta, -2.0 * c / d);
+                    const double a = pos * f, co = cos(a), si = sin(a);
+                    const double x0 = load_elem(x, dtype, row + c), x1 = load_elem(x, dtype, row + c + h);
+                    out[row + c] = x0 * co - x1 * si;
+                    out[row + c + h] = x1 * co + x0 * si;
+                }
+            }
+        }
+    return 0;
+}

@@ -55,6 +55,13 @@ MUTANTS = [
      [lambda o: pins.test_bwd_invariants(o, CROSS, 0), pins.test_bwd_zero_query_closed_form]),
     ("bwd key rows skip their own query", "for (int64_t t = tk; t < nL; ++t) {",
      "for (int64_t t = tk + 1; t < nL; ++t) {", [pins.test_bwd_window1_closed_form]),
+    ("rope rotates the wrong way", "out[row + c] = x0 * co - x1 * si;", "out[row + c] = x0 * co + x1 * si;",
+     [pins.test_rope_matches_transformers_rotate_half, pins.test_rope_golden_d4]),
+    ("rope frequency exponent off by one", "const double f = pow(theta, -2.0 * c / d);",
+     "const double f = pow(theta, -2.0 * (c + 1) / d);",
+     [pins.test_rope_matches_transformers_rotate_half, pins.test_rope_golden_d4]),
+    ("rope decode position ignores the stream", "const double pos = (double)t + (pos_base ?",
+     "const double pos = (double)0 * t + (pos_base ?", [pins.test_rope_decode_positions]),
 ]
 
 

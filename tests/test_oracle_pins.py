@@ -469,3 +469,65 @@ def test_bwd_rows_subset_matches_full(oracle):
     np.testing.assert_array_equal(sq, dq.reshape(-1, d)[qrows])
     np.testing.assert_array_equal(sk, dk.reshape(-1, d)[krows])
     np.testing.assert_array_equal(sv, dv.reshape(-1, d)[krows])
+
+
+# --------------------------------------------------------------------------
+# Rotary embedding at the expanded (contiguous) positions
+# --------------------------------------------------------------------------
+
+def test_rope_matches_transformers_rotate_half(oracle):
+    """Library pin: transformers' Llama apply_rotary_pos_emb / rotate_half with
+    inv_freq = theta^(-2c/d) and positions 0..T-1, in float64."""
+    from transformers.models.llama.modeling_llama import apply_rotary_pos_emb
+    B, T, H, d, theta = 2, 11, 3, 16, 500.0
+    x = _rand((B, T, H, d), 51)
+    got = oracle.rope(x, theta)
+    inv = 1.0 / (theta ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    ang = torch.arange(T, dtype=torch.float64)[:, None] * inv[None, :]
+    emb = torch.cat([ang, ang], dim=-1)
+    cos, sin = emb.cos()[None], emb.sin()[None]                    # [1, T, d]
+    xt = x.double().permute(0, 2, 1, 3)                            # [B, H, T, d]
+    want, _ = apply_rotary_pos_emb(xt, xt, cos, sin, unsqueeze_dim=1)
+    np.testing.assert_allclose(got, want.permute(0, 2, 1, 3).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rope_golden_d4(oracle):
+    """Hand-worked: d=4, theta=100 -> frequencies 1 and 0.1; position 1."""
+    x = torch.tensor([[[[0.0, 0.0, 0.0, 0.0]], [[1.0, 2.0, 3.0, 4.0]]]])   # T=2, position 1 is row 1
+    got = oracle.rope(x, 100.0)[0, 1, 0]
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.1), math.sin(0.1)
+    want = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+
+
+def test_rope_relative_position_and_norm(oracle):
+    """q(t1).k(t2) depends only on t1 - t2; position 0 is the identity;
+    each (c, c + d/2) pair keeps its norm."""
+    d, theta = 32, 10000.0
+    q = _rand((1, 1, 1, d), 52)
+    k = _rand((1, 1, 1, d), 53)
+    T = 40
+    qs = oracle.rope(q.expand(1, T, 1, d).contiguous(), theta)[0, :, 0]
+    ks = oracle.rope(k.expand(1, T, 1, d).contiguous(), theta)[0, :, 0]
+    for t1, t2, s in ((7, 3, 20), (30, 30, 5), (2, 9, 17)):
+        if t1 + s < T and t2 + s < T:
+            assert abs(qs[t1] @ ks[t2] - qs[t1 + s] @ ks[t2 + s]) < 1e-12
+    np.testing.assert_allclose(qs[0], q[0, 0, 0].double().numpy(), rtol=0, atol=0)
+    h = d // 2
+    qn = q[0, 0, 0].double().numpy()
+    for t in (1, 13, 39):
+        np.testing.assert_allclose(qs[t][:h] ** 2 + qs[t][h:] ** 2, qn[:h] ** 2 + qn[h:] ** 2, rtol=1e-12)
+
+
+def test_rope_decode_positions(oracle):
+    """pos_base/pos_mul place stream s of the new token at len*n + s: equal to
+    the rows len*n + s of a prefill rotation."""
+    n, H, d = 4, 2, 16
+    lens = [5, 0, 12]
+    x = _rand((3, n, H, d), 54)
+    got = oracle.rope(x, 10000.0, pos_base=lens, pos_mul=n)
+    for b, ln in enumerate(lens):
+        full = torch.zeros(1, (ln + 1) * n, H, d)
+        full[0, ln * n:] = x[b]
+        want = oracle.rope(full, 10000.0)[0, ln * n:]
+        np.testing.assert_allclose(got[b], want, rtol=1e-13, atol=1e-13)
