@@ -6,6 +6,7 @@ are already resident in HBM:
   intra prefill  n=4, L=4096 (nL=16384), 32 q / 8 kv heads, d=128, bf16   <- headline
   intra prefill  n=1, L=4096 control (for the n=4 / n=1 time ratio)
   cross prefill  same shapes as the headline, dense causal over 16384 positions
+  rotary embed   q and k of the headline layer at the expanded positions
   backward       dQ, dK, dV of the headline intra-stream layer (given o, lse, dO)
   decode         64 sequences, 8192 cached tokens x 4 streams, 32 q / 8 kv heads,
                  intra and cross (one new token, 4 stream queries each)
@@ -189,6 +190,16 @@ def main():
 
     if want("bwd_intra_n4"):
         comps["bwd_intra_n4"] = backward(I)
+    if want("rope_qk"):
+        # rotary embedding of the headline layer's q and k at the expanded
+        # positions (in place); bytes = read + write of q and k
+        q, k, _ = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+
+        def run_rope(q=q, k=k):
+            hd.hd_rope(q, q, 10000.0)
+            hd.hd_rope(k, k, 10000.0)
+
+        comps["rope_qk"] = (run_rope, 0.0, 2 * 2 * (q.numel() + k.numel()))
     if want("decode_intra") or want("decode_cross"):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)

@@ -74,6 +74,26 @@ hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n,
                           void *out, void *stream);
 
 /*
+ * Rotary position embedding at the expanded positions ("Multi-Stream
+ * Expansion and Training Objective": the expanded sequence is fed to the
+ * Transformer with contiguous RoPE positions, so S_t is rotated by its
+ * expanded position t = i*n + s, not by its token index).  Rotate-half form,
+ * h = d/2, f_c = theta^(-2c/d):
+ *   out[..][c]     = x[c] cos(p f_c) - x[c+h] sin(p f_c)
+ *   out[..][c + h] = x[c+h] cos(p f_c) + x[c] sin(p f_c)
+ * with position p = t + pos_mul * pos_base[b] for row (b, t).
+ *   x, out    [B][T][H][d] (dtype dt); out may equal x (in place)
+ *   pos_base  device int32 [B] or NULL (0): prefill of the expanded sequence
+ *             passes NULL (p = t); a decode step passes q or k_new as
+ *             [B][n][H][d] with pos_base = cache_len and pos_mul = n, so
+ *             stream s of the new token gets p = len*n + s
+ * Apply it to q and k before hd_sfa_fwd / hd_sfa_decode.  Requires B, T, H >= 1,
+ * d in {32, 64, 128}, theta > 0, pos_mul >= 0.
+ */
+hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,
+                  float theta, hd_dtype dt, void *stream);
+
+/*
  * Stream-Factorized Attention prefill ("Stream-Factorized Attention", index
  * maps i(t) = ceil(t/n), s(t) = (t-1) mod n + 1, and Figure 2).  For every
  * query row (b, t_q, h) with i_q = t_q/n, s_q = t_q%n:

@@ -132,6 +132,25 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
     return device_status(e, "sfa_fwd launch");
 }
 
+hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,
+                  float theta, hd_dtype dt, void *stream) {
+    if (B < 1 || T < 1 || H < 1) return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d T=%d H=%d)", B, T, H);
+    if (d != 32 && d != 64 && d != 128) return fail(HD_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
+    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (!(theta > 0.f) || !std::isfinite(theta)) return fail(HD_ERR_INVALID, "theta=%g must be > 0", (double)theta);
+    if (pos_mul < 0) return fail(HD_ERR_INVALID, "pos_mul=%lld < 0", (long long)pos_mul);
+    HD_TRY(check_ptr(x, "x"));
+    HD_TRY(check_ptr(out, "out"));
+    if (pos_base != nullptr && (reinterpret_cast<uintptr_t>(pos_base) & 3u))
+        return fail(HD_ERR_INVALID, "pos_base is not 4-byte aligned");
+    hd::RopeArgs a{};
+    a.x = x; a.out = out; a.pos_base = pos_base; a.pos_mul = pos_mul;
+    a.B = B; a.T = T; a.H = H; a.d = d;
+    for (int c = 0; c < d / 2; ++c)
+        a.freq_turns[c] = std::pow((double)theta, -2.0 * c / d) / (2.0 * 3.14159265358979323846);
+    return device_status(hd::launch_rope(a, dt == HD_BF16, static_cast<hipStream_t>(stream)), "rope launch");
+}
+
 size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
     if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
     if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;

@@ -67,6 +67,18 @@ hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
+// Rotary embedding of x [B][T][H][d] at positions t + pos_mul * pos_base[b].
+struct RopeArgs {
+    const void *x;
+    void *out;                // may equal x
+    const int32_t *pos_base;  // device [B] or NULL
+    int64_t pos_mul;
+    int B, T, H, d;
+    double freq_turns[64];    // theta^(-2c/d) / (2 pi), c < d/2
+};
+hipError_t launch_rope(const RopeArgs &a, bool bf16_data, hipStream_t st);
+
+// ---------------------------------------------------------------------------
 // Decode over the per-stream cache [B][T_cap][n][Hkv][d].
 struct DecArgs {
     const void *q, *k_new, *v_new;

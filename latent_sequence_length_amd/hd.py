@@ -45,7 +45,8 @@ def load():
     lib.hd_sfa_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.hd_sfa_bwd_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
-    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_decode, lib.hd_sfa_bwd):
+    lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
+    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_decode, lib.hd_sfa_bwd, lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -168,6 +169,21 @@ def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=
     return o
 
 
+def hd_rope(x, out, theta=10000.0, pos_base=None, pos_mul=0):
+    """Rotary embedding of x [B, T, H, d] at positions t + pos_mul*pos_base[b] into out (may be x)."""
+    B, T, H, d = x.shape
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x in shape and dtype")
+    pb = None
+    if pos_base is not None:
+        if pos_base.shape != (B,):
+            raise ValueError("pos_base must be [B]")
+        pb = _dev(pos_base, "pos_base", torch.int32)
+    _check(load().hd_rope(_dev(x, "x"), _dev(out, "out"), B, T, H, d, pb, int(pos_mul), float(theta),
+                          _dtype_code(x), _stream(x)))
+    return out
+
+
 def hd_sfa_bwd_workspace_bytes(B, L, n, Hq, Hkv, d, dtype=torch.bfloat16):
     return int(load().hd_sfa_bwd_workspace_bytes(B, L, n, Hq, Hkv, d, _DT[dtype]))
 
@@ -226,3 +242,7 @@ def sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, sca
 def sfa_bwd(q, k, v, o, dout, lse, n, mode, window=0, scale=0.0):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     return hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window, scale)
+
+
+def rope(x, theta=10000.0, pos_base=None, pos_mul=0):
+    return hd_rope(x, torch.empty_like(x), theta, pos_base, pos_mul)

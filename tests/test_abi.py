@@ -32,7 +32,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "hd_expand_embed", "hd_sfa_fwd", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
         "hd_status_string", "hd_last_error", "hd_version"])
 
@@ -131,6 +131,19 @@ def test_bwd_workspace_size(lib):
     assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4
     assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4
     assert f(0, 8, 2, 4, 2, 64) == 0 and f(1, 8, 2, 4, 3, 64) == 0 and f(1, 8, 2, 4, 2, 96) == 0
+
+
+def test_rope_validation(lib):
+    f = lib.hd_rope
+    ok = dict(x=FAKE, out=FAKE, B=1, T=8, H=2, d=64, pos_base=None, pos_mul=0, theta=10000.0, dt=0, stream=None)
+    for kw, code in [(dict(B=0), hd.HD_ERR_INVALID), (dict(T=0), hd.HD_ERR_INVALID), (dict(d=48), hd.HD_ERR_UNSUPPORTED),
+                     (dict(theta=0.0), hd.HD_ERR_INVALID), (dict(theta=-1.0), hd.HD_ERR_INVALID),
+                     (dict(pos_mul=-1), hd.HD_ERR_INVALID), (dict(x=None), hd.HD_ERR_INVALID),
+                     (dict(out=FAKE + 2), hd.HD_ERR_INVALID), (dict(pos_base=FAKE + 2), hd.HD_ERR_INVALID),
+                     (dict(dt=9), hd.HD_ERR_UNSUPPORTED)]:
+        a = dict(ok)
+        a.update(kw)
+        assert f(*a.values()) == code, kw
 
 
 def test_embed_validation(lib):
