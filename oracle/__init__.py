@@ -18,6 +18,9 @@ maps i(t) = ceil(t/n), s(t) = (t-1) mod n + 1 and Figure 2's three masks; the
 per-stream KV cache retained for decoding.
 
 The backward (``sfa_bwd*``) is the chain-rule derivative of that forward.
+``sfa_final*`` computes only the final stream's query rows (section
+"Persistent KV and the KV-mirror Saving": mirrored layers run the last stream
+alone over K/V of every stream).
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against library
 routines, closed forms, invariants, finite differences and hand-worked golden
@@ -59,6 +62,8 @@ def _configure(lib):
     lib.oracle_visible.argtypes = [I64, I64, I, I, I64]
     lib.oracle_sfa_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, I64, P, P]
     lib.oracle_sfa_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
+    lib.oracle_sfa_final_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, I64, P, P]
+    lib.oracle_sfa_final.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
     lib.oracle_sfa_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, I64, D, P]
     lib.oracle_decode_append.argtypes = [P, P, P, I, I, I, I, I, I64]
     lib.oracle_sfa_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P, P, I64, P, P, I64, P, P]
@@ -164,6 +169,46 @@ def sfa_fwd(q, k, v, n, mode, window=0, scale=0.0):
                                 int(mode), int(window), float(scale), _p(o), _p(lse))
     if rc:
         raise ValueError("oracle_sfa_fwd rejected its arguments")
+    return o, lse
+
+
+def _final_shapes(qf, k, v, n):
+    qb, dt = _buf(qf)
+    kb, dt2 = _buf(k)
+    vb, dt3 = _buf(v)
+    if not (dt == dt2 == dt3):
+        raise TypeError("qf, k, v must share a dtype")
+    B, L, Hq, d = qb.shape
+    if kb.shape[0] != B or kb.shape[1] != n * L or kb.shape[3] != d or vb.shape != kb.shape:
+        raise ValueError("k/v must be [B, n*L, Hkv, d] for qf [B, L, Hq, d]")
+    return qb, kb, vb, dt, B, L, Hq, kb.shape[2], d
+
+
+def sfa_final_rows(qf, k, v, n, mode, window=0, scale=0.0, rows=None):
+    """Final-stream queries of a KV-mirror layer, for selected flat rows
+    r = (b*L + i)*Hq + h of qf [B, L, Hq, d] (query i at expanded position
+    i*n + n-1); k/v [B, n*L, Hkv, d].  Returns (o [nrows, d], lse [nrows])."""
+    qb, kb, vb, dt, B, L, Hq, Hkv, d = _final_shapes(qf, k, v, n)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    rc = _load().oracle_sfa_final_rows(_p(qb), _p(kb), _p(vb), dt, B, L, n, Hq, Hkv, d,
+                                       int(mode), int(window), float(scale), _p(rows), rows.size,
+                                       _p(o), _p(lse))
+    if rc:
+        raise ValueError("oracle_sfa_final_rows rejected its arguments")
+    return o, lse
+
+
+def sfa_final(qf, k, v, n, mode, window=0, scale=0.0):
+    """All final-stream queries: (o [B, L, Hq, d], lse [B, Hq, L]), float64."""
+    qb, kb, vb, dt, B, L, Hq, Hkv, d = _final_shapes(qf, k, v, n)
+    o = np.empty((B, L, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, L), dtype=np.float64)
+    rc = _load().oracle_sfa_final(_p(qb), _p(kb), _p(vb), dt, B, L, n, Hq, Hkv, d,
+                                  int(mode), int(window), float(scale), _p(o), _p(lse))
+    if rc:
+        raise ValueError("oracle_sfa_final rejected its arguments")
     return o, lse
 
 

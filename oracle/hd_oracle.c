@@ -191,6 +191,74 @@ int oracle_sfa_fwd(const void *q, const void *k, const void *v, int dtype,
 }
 
 /* ---------------------------------------------------------------------------
+ * Final-stream queries of a KV-mirror layer ("Persistent KV and the KV-mirror
+ * Saving": a mirrored layer's K/V come from an earlier layer's hidden states,
+ * where every stream was processed, and only the last stream, the supervised
+ * one, is run through the mirrored layer).  Its queries are the rows of stream
+ * n-1: query i sits at expanded position t = i*n + (n-1) and attends over the
+ * K/V of all n*L positions under the layer's own mask (intra: stream n-1
+ * only; cross: every position up to t), exactly as that row of the full layer.
+ *
+ * qf [B][L][Hq][d] (final-stream rows only), k/v [B][n*L][Hkv][d].
+ * rows: flat ids into qf, r = (b*L + i)*Hq + h.  Outputs o [nrows][d],
+ * lse [nrows].  Returns 0, or -1 on bad arguments.
+ * ------------------------------------------------------------------------- */
+int oracle_sfa_final_rows(const void *qf, const void *k, const void *v, int dtype,
+                          int B, int L, int n, int Hq, int Hkv, int d, int mode,
+                          int64_t W, double scale, const int64_t *rows, int64_t nrows,
+                          double *o, double *lse) {
+    if (B < 1 || L < 1 || n < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv) return -1;
+    if (W < 0 || (mode != OR_INTRA && mode != OR_CROSS)) return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    const int64_t nL = (int64_t)n * L;
+    const int g = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *scores = (double *)malloc(sizeof(double) * (size_t)nL);
+        int64_t *kpos = (int64_t *)malloc(sizeof(int64_t) * (size_t)nL);
+        int64_t *koff = (int64_t *)malloc(sizeof(int64_t) * (size_t)nL);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t id = rows[r];
+            if (id < 0 || id >= (int64_t)B * L * Hq) { bad = 1; continue; }
+            int64_t h = id % Hq, i = (id / Hq) % L, b = id / Hq / L;
+            int64_t hk = h / g;
+            int64_t t = i * n + (n - 1);   /* the final stream's expanded position */
+            int64_t nk = t + 1;            /* every mask is causal: t_k <= t */
+            for (int64_t tk = 0; tk < nk; ++tk) {
+                kpos[tk] = tk;
+                koff[tk] = ((b * nL + tk) * Hkv + hk) * d;
+            }
+            attend_row(qf, id * d, k, v, koff, kpos, nk, t, n, mode, W, d, dtype,
+                       scale, scores, o + r * d, lse ? lse + r : NULL);
+        }
+        free(scores); free(kpos); free(koff);
+    }
+    return bad ? -1 : 0;
+}
+
+/* All final-stream rows: o [B][L][Hq][d] (double), lse [B][Hq][L] (may be NULL). */
+int oracle_sfa_final(const void *qf, const void *k, const void *v, int dtype,
+                     int B, int L, int n, int Hq, int Hkv, int d, int mode,
+                     int64_t W, double scale, double *o, double *lse) {
+    const int64_t total = (int64_t)B * L * Hq;
+    int64_t *rows = (int64_t *)malloc(sizeof(int64_t) * (size_t)total);
+    double *lrow = lse ? (double *)malloc(sizeof(double) * (size_t)total) : NULL;
+    for (int64_t r = 0; r < total; ++r) rows[r] = r;
+    int rc = oracle_sfa_final_rows(qf, k, v, dtype, B, L, n, Hq, Hkv, d, mode, W, scale,
+                                   rows, total, o, lrow);
+    if (rc == 0 && lse) {
+        for (int64_t r = 0; r < total; ++r) {  /* [b][i][h] -> [b][h][i] */
+            int64_t h = r % Hq, i = (r / Hq) % L, b = r / Hq / L;
+            lse[(b * Hq + h) * L + i] = lrow[r];
+        }
+    }
+    free(rows); free(lrow);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------
  * Decode step over the retained per-stream KV cache ("Persistent KV ...",
  * "Inference Throughput").  For each sequence b with len = cache_len[b] tokens
  * already cached, the new token's n stream keys/values are appended at token

@@ -62,6 +62,16 @@ MUTANTS = [
      [pins.test_rope_matches_transformers_rotate_half, pins.test_rope_golden_d4]),
     ("rope decode position ignores the stream", "const double pos = (double)t + (pos_base ?",
      "const double pos = (double)0 * t + (pos_base ?", [pins.test_rope_decode_positions]),
+    ("final query placed at stream 0", "int64_t t = i * n + (n - 1);   /* the final stream's expanded position */",
+     "int64_t t = i * n;   /* the final stream's expanded position */",
+     [lambda o: pins.test_final_matches_sdpa_with_onebased_rows(o, CROSS, 0), pins.test_final_closed_forms]),
+    ("final keys stop before the token's other streams",
+     "int64_t nk = t + 1;            /* every mask is causal: t_k <= t */",
+     "int64_t nk = i * n + 1;            /* every mask is causal: t_k <= t */",
+     [lambda o: pins.test_final_matches_sdpa_with_onebased_rows(o, CROSS, 0),
+      lambda o: pins.test_final_equals_full_layer_last_stream_rows(o, CROSS, 2)]),
+    ("final lse stored query-major", "lse[(b * Hq + h) * L + i] = lrow[r];", "lse[(b * L + i) * Hq + h] = lrow[r];",
+     [lambda o: pins.test_final_matches_sdpa_with_onebased_rows(o, INTRA, 2)]),
 ]
 
 

@@ -531,3 +531,94 @@ def test_rope_decode_positions(oracle):
         full[0, ln * n:] = x[b]
         want = oracle.rope(full, 10000.0)[0, ln * n:]
         np.testing.assert_allclose(got[b], want, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Final-stream queries of a KV-mirror layer
+# --------------------------------------------------------------------------
+
+def _final_inputs(B, L, n, Hq, Hkv, d, seed=60):
+    qf = _rand((B, L, Hq, d), seed)
+    k = _rand((B, n * L, Hkv, d), seed + 1)
+    v = _rand((B, n * L, Hkv, d), seed + 2)
+    return qf, k, v
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (INTRA, 2), (CROSS, 3), (CROSS, 1)])
+def test_final_matches_sdpa_with_onebased_rows(oracle, mode, W):
+    """Library pin: torch SDPA (float64) with the rectangular mask made of the
+    rows of the 1-based Figure 2 mask at t = i*n (the last stream of token i);
+    lse against torch.logsumexp of the same masked scores."""
+    B, L, n, Hq, Hkv, d = 2, 7, 3, 4, 2, 16
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d)
+    full = brute.mask(n, L, mode, W)
+    rows = np.array([i * n - 1 for i in range(1, L + 1)])     # 1-based t = i*n  ->  0-based row i*n - 1
+    m = torch.from_numpy(full[rows])                           # [L, nL]
+    want = sdpa64(qf, k, v, attn_mask=m)
+    got, lse = oracle.sfa_final(qf, k, v, n, mode, W)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+    s = torch.einsum("bihc,bjhc->bhij", qf.double(), k.double().repeat_interleave(Hq // Hkv, dim=2)) / math.sqrt(d)
+    want_lse = torch.logsumexp(s.masked_fill(~m, -math.inf), dim=-1)
+    np.testing.assert_allclose(lse, want_lse.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_final_intra_is_causal_on_last_stream(oracle):
+    """Intra mirrored layer: causal attention of the final-stream queries over
+    the final stream's keys alone (rows n-1, 2n-1, ... of K/V)."""
+    B, L, n, Hq, Hkv, d = 1, 9, 4, 2, 1, 8
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d, seed=63)
+    got, _ = oracle.sfa_final(qf, k, v, n, INTRA)
+    want = sdpa64(qf, k[:, n - 1::n], v[:, n - 1::n], causal=True)
+    np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [INTRA, CROSS])
+def test_final_n1_is_textbook_causal(oracle, mode):
+    qf, k, v = _final_inputs(2, 11, 1, 2, 2, 8, seed=66)
+    got, _ = oracle.sfa_final(qf, k, v, 1, mode)
+    np.testing.assert_allclose(got, sdpa64(qf, k, v, causal=True).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_final_closed_forms(oracle):
+    """Zero queries give uniform weights: cross sees the (i+1)*n positions of
+    tokens 0..i (lse = log((i+1)n)); cross with W=1 sees the n streams of token
+    i only; intra with W=1 returns the final-stream value row itself."""
+    B, L, n, Hq, Hkv, d = 1, 6, 3, 2, 1, 4
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d, seed=69)
+    zero = torch.zeros_like(qf)
+    v64 = v.double().numpy()[0, :, 0]
+    o, lse = oracle.sfa_final(zero, k, v, n, CROSS)
+    for i in range(L):
+        np.testing.assert_allclose(o[0, i, 0], v64[:(i + 1) * n].mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(lse[0, 1, i] - math.log((i + 1) * n)) < 1e-13
+    o, lse = oracle.sfa_final(zero, k, v, n, CROSS, 1)
+    for i in range(L):
+        np.testing.assert_allclose(o[0, i, 1], v64[i * n:(i + 1) * n].mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(lse[0, 0, i] - math.log(n)) < 1e-13
+    o, _ = oracle.sfa_final(qf, k, v, n, INTRA, 1)
+    for i in range(L):
+        np.testing.assert_array_equal(o[0, i, 0], v64[i * n + n - 1])
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (CROSS, 2), (INTRA, 3)])
+def test_final_equals_full_layer_last_stream_rows(oracle, mode, W):
+    """Running the final stream alone changes nothing for it: its rows equal
+    rows n-1, 2n-1, ... of the full layer whatever the other streams' queries."""
+    B, L, n, Hq, Hkv, d = 2, 5, 3, 4, 2, 8
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d, seed=72)
+    q = _rand((B, n * L, Hq, d), 75)
+    q[:, n - 1::n] = qf
+    o_full, lse_full = oracle.sfa_fwd(q, k, v, n, mode, W)
+    o, lse = oracle.sfa_final(qf, k, v, n, mode, W)
+    np.testing.assert_allclose(o, o_full[:, n - 1::n], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lse_full[:, :, n - 1::n], rtol=1e-13, atol=1e-13)
+
+
+def test_final_rows_subset_matches_full(oracle):
+    B, L, n, Hq, Hkv, d = 2, 6, 2, 4, 2, 8
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d, seed=78)
+    o, lse = oracle.sfa_final(qf, k, v, n, CROSS, 2)
+    rows = np.array([0, 5, 17, B * L * Hq - 1])
+    so, sl = oracle.sfa_final_rows(qf, k, v, n, CROSS, 2, rows=rows)
+    np.testing.assert_array_equal(so, o.reshape(-1, d)[rows])
+    np.testing.assert_array_equal(sl, lse.transpose(0, 2, 1).reshape(-1)[rows])
