@@ -223,12 +223,12 @@ int oracle_sfa_final_rows(const void *qf, const void *k, const void *v, int dtyp
             int64_t id = rows[r];
             if (id < 0 || id >= (int64_t)B * L * Hq) { bad = 1; continue; }
             int64_t h = id % Hq, i = (id / Hq) % L, b = id / Hq / L;
-            int64_t hk = h / g;
+            int64_t kvh = h / g;
             int64_t t = i * n + (n - 1);   /* the final stream's expanded position */
             int64_t nk = t + 1;            /* every mask is causal: t_k <= t */
             for (int64_t tk = 0; tk < nk; ++tk) {
                 kpos[tk] = tk;
-                koff[tk] = ((b * nL + tk) * Hkv + hk) * d;
+                koff[tk] = ((b * nL + tk) * Hkv + kvh) * d;
             }
             attend_row(qf, id * d, k, v, koff, kpos, nk, t, n, mode, W, d, dtype,
                        scale, scores, o + r * d, lse ? lse + r : NULL);
