@@ -47,6 +47,18 @@ def useful_flops(B, L, n, Hq, d, mode, window=0):
     return 4.0 * d * Hq * B * pairs
 
 
+def useful_flops_final(B, L, n, Hq, d, mode, window=0):
+    """Final-stream queries of a KV-mirror layer: query i sees tokens
+    j <= i (within the window) of stream n-1 only (intra) or of all n
+    streams (cross)."""
+    def tri(T, w):
+        if w <= 0 or w >= T:
+            return T * (T + 1) // 2
+        return w * (w + 1) // 2 + (T - w) * w
+    pairs = tri(L, window) * (n if mode == 1 else 1)
+    return 4.0 * d * Hq * B * pairs
+
+
 def measured_traffic(name):
     """HBM bytes per launch of a kernel from its committed PMC summary
     (profiles/<name>.md: FETCH_SIZE + WRITE_SIZE scaled by a copy kernel), or
@@ -170,6 +182,25 @@ def main():
         comps["intra_n1"] = prefill(I1)
     if want("cross_n4"):
         comps["cross_n4"] = prefill(X)
+    def final(cfg):
+        """Final-stream queries (rows t = i*n + n-1 only, compact) of the
+        layer's shapes over K/V of every stream; bytes = q, o of the final
+        stream + the K/V rows the mask reaches (all for cross, stream n-1's
+        for intra)."""
+        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+        qf = q[:, cfg.n - 1::cfg.n].contiguous()
+        del q
+        o = torch.empty_like(qf)
+        fl = useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+        kv = (k.numel() + v.numel()) // (cfg.n if cfg.mode == 0 else 1)
+        by = 2 * (2 * qf.numel() + kv)
+        return (lambda: hd.hd_sfa_fwd_final(qf, k, v, o, cfg.n, cfg.mode, cfg.window), fl, by)
+
+    if want("final_cross_n4"):
+        comps["final_cross_n4"] = final(X)
+    if want("final_intra_n4"):
+        comps["final_intra_n4"] = final(I)
+
     def backward(cfg):
         """(callable, useful flops, algorithmic bytes) of one backward call of
         the layer; o and lse come from one forward call outside the timed

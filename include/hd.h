@@ -113,6 +113,23 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
                      hd_mode mode, int window, float scale, hd_dtype dt, void *stream);
 
 /*
+ * Final-stream queries of a KV-mirror layer ("Persistent KV and the KV-mirror
+ * Saving": a mirrored layer takes its K/V from an earlier layer, where all n
+ * streams were processed, and only the supervised last stream is run through
+ * it).  Query i of q is the row of stream n-1 of token i, expanded position
+ * t = i*n + n-1; it attends over k/v of all n*L positions exactly as that row
+ * of hd_sfa_fwd would:
+ *   mode HD_MODE_INTRA: keys t_k = j*n + n-1, j <= i, i - j < window if > 0;
+ *   mode HD_MODE_CROSS: keys t_k <= t, t - t_k < n*window if window > 0.
+ *   q, o  [B][L][Hq][d] (final-stream rows only)   k, v  [B][n*L][Hkv][d]
+ *   lse   optional float32 [B][Hq][L] (NULL = skip)
+ * Same requirements and errors as hd_sfa_fwd.
+ */
+hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o, float *lse,
+                           int B, int L, int n, int Hq, int Hkv, int d,
+                           hd_mode mode, int window, float scale, hd_dtype dt, void *stream);
+
+/*
  * Bytes of device workspace hd_sfa_bwd needs for these sizes (0 if the sizes
  * are invalid): one float32 per query row, B*Hq*n*L*4.
  */

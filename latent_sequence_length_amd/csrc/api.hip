@@ -127,9 +127,48 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
     }
     if (mode == HD_MODE_INTRA && window >= L) a.weff = 0;  // window covers everything
     a.scale = resolve_scale(scale, d);
+    // every position is a query, its Q row laid out like its K row
+    a.kbase = 0;
+    a.Lq = a.Lsub; a.qrows = n * L; a.qsub = 1; a.qstride = a.stride;
+    a.qmul = 1; a.qadd = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
     return device_status(e, "sfa_fwd launch");
+}
+
+hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o, float *lse, int B, int L, int n,
+                           int Hq, int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt,
+                           void *stream) {
+    if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
+    HD_TRY(check_ptr(q, "q"));
+    HD_TRY(check_ptr(k, "k"));
+    HD_TRY(check_ptr(v, "v"));
+    HD_TRY(check_ptr(o, "o"));
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
+    hd::FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    a.nsub = 1;
+    a.Lq = L; a.qrows = L; a.qsub = 0; a.qstride = 1;  // query i is row i of the compact q
+    if (mode == HD_MODE_INTRA) {
+        // stream n-1's own sub-sequence: key j at position j*n + n-1
+        a.Lsub = L; a.stride = n; a.kbase = n - 1;
+        a.qmul = 1; a.qadd = 0;
+        a.weff = (window >= L) ? 0 : window;
+    } else {
+        // the whole expanded sequence; query i sits at position i*n + n-1
+        a.Lsub = n * L; a.stride = 1; a.kbase = 0;
+        a.qmul = n; a.qadd = n - 1;
+        const int64_t w = (int64_t)n * window;
+        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
+    }
+    a.scale = resolve_scale(scale, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
+    return device_status(e, "sfa_fwd_final launch");
 }
 
 hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,

@@ -35,18 +35,29 @@ hipError_t launch_expand_embed(const EmbedArgs &a, hipStream_t st);
 //          length L, window W tokens;
 //   cross: one sub-sequence (the whole expanded sequence), element j at
 //          position j, length n*L, window n*W positions.
-// A key j is visible to query i of the same sub-sequence iff
-//   j <= i  and  (weff == 0 || i - j < weff).
+// Query p of a sub-sequence sees key element j iff
+//   j <= lim(p) = p*qmul + qadd  and  (weff == 0 || lim(p) - j < weff).
+// A full layer has one query per key element (qmul = 1, qadd = 0, Q rows laid
+// out like K rows).  The final-stream queries of a KV-mirror layer are the
+// rows t = p*n + n-1 only, stored compactly: intra runs stream n-1's
+// sub-sequence (kbase = n-1) with lim(p) = p; cross runs the whole sequence
+// with lim(p) = p*n + n-1.
 struct FwdArgs {
     const void *q, *k, *v;
     void *o;
-    float *lse;
+    float *lse;   // [B][Hq][qrows]
     int B, nL, Hq, Hkv, d;
-    int Lsub;     // elements per sub-sequence
+    int Lsub;     // key elements per sub-sequence
     int nsub;     // sub-sequences per batch row (n for intra, 1 for cross)
-    int stride;   // expanded positions between consecutive elements
+    int stride;   // expanded positions between consecutive key elements
+    int kbase;    // expanded position of element 0 of sub-sequence 0
     int weff;     // window in sub-sequence elements, 0 = none
     float scale;  // softmax scale (already resolved, > 0)
+    int Lq;       // queries per sub-sequence
+    int qrows;    // Q / O / lse rows per batch row
+    int qsub;     // Q rows between the first queries of consecutive sub-sequences
+    int qstride;  // Q rows between consecutive queries
+    int qmul, qadd;
 };
 hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st);

@@ -16,27 +16,29 @@ namespace {
 template <int D>
 __global__ __launch_bounds__(64) void sfa_fwd_f32_kernel(FwdArgs p) {
     const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, sub, i, h)
-    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lsub * p.Hq;
+    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lq * p.Hq;
     if (row >= nrows) return;
     const int h = (int)(row % p.Hq);
     int64_t r = row / p.Hq;
-    const int i = (int)(r % p.Lsub); r /= p.Lsub;
+    const int i = (int)(r % p.Lq); r /= p.Lq;
     const int sub = (int)(r % p.nsub);
     const int b = (int)(r / p.nsub);
     const int kvh = h / (p.Hq / p.Hkv);
-    const int64_t bpos = (int64_t)b * p.nL + sub;
+    const int64_t kpos0 = (int64_t)b * p.nL + p.kbase + sub;  // key element 0
+    const int64_t qrow = (int64_t)b * p.qrows + (int64_t)sub * p.qsub + (int64_t)i * p.qstride;
     const float *qg = static_cast<const float *>(p.q);
     const float *kg = static_cast<const float *>(p.k);
     const float *vg = static_cast<const float *>(p.v);
 
     float qv[D], acc[D];
-    const float *qp = qg + ((bpos + (int64_t)i * p.stride) * p.Hq + h) * D;
+    const float *qp = qg + (qrow * p.Hq + h) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) { qv[c] = qp[c]; acc[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
-    const int jbeg = p.weff ? max(0, i - p.weff + 1) : 0;
-    for (int j = jbeg; j <= i; ++j) {
-        const int64_t off = ((bpos + (int64_t)j * p.stride) * p.Hkv + kvh) * D;
+    const int lim = i * p.qmul + p.qadd;  // last visible key element
+    const int jbeg = p.weff ? max(0, lim - p.weff + 1) : 0;
+    for (int j = jbeg; j <= lim; ++j) {
+        const int64_t off = ((kpos0 + (int64_t)j * p.stride) * p.Hkv + kvh) * D;
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < D; ++c) s = fmaf(qv[c], kg[off + c], s);
@@ -49,12 +51,11 @@ __global__ __launch_bounds__(64) void sfa_fwd_f32_kernel(FwdArgs p) {
         for (int c = 0; c < D; ++c) acc[c] = fmaf(e, vg[off + c], acc[c] * alpha);
         m = mn;
     }
-    const int64_t pos = bpos + (int64_t)i * p.stride;
-    float *op = static_cast<float *>(p.o) + (pos * p.Hq + h) * D;
+    float *op = static_cast<float *>(p.o) + (qrow * p.Hq + h) * D;
     const float inv = 1.f / l;
 #pragma unroll
     for (int c = 0; c < D; ++c) op[c] = acc[c] * inv;
-    if (p.lse != nullptr) p.lse[((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL)] = m + logf(l);
+    if (p.lse != nullptr) p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] = m + logf(l);
 }
 
 // Decode: one thread per (b, s, h) query; also appends the new rows.
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void append_f32_kernel(DecArgs p) {
 }  // namespace
 
 hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st) {
-    const int64_t nrows = (int64_t)a.B * a.nsub * a.Lsub * a.Hq;
+    const int64_t nrows = (int64_t)a.B * a.nsub * a.Lq * a.Hq;
     const int64_t grid = (nrows + 63) / 64;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     switch (a.d) {

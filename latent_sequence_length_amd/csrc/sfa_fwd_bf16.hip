@@ -68,11 +68,15 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
     const int h = kvh * g + hgrp * HG + hw;
     const int qw0 = q0 + tb * QW;       // first query of this wave
     const int myq = qw0 + l32;          // this lane's query (sub-sequence index)
-    const bool qvalid = myq < p.Lsub;
+    const bool qvalid = myq < p.Lq;
+    const int mylim = myq * p.qmul + p.qadd;                      // last key this query may see
+    const int lim0 = qw0 * p.qmul + p.qadd;                       // ... for the wave's first query
+    const int lim1 = (qw0 + QW - 1) * p.qmul + p.qadd;            // ... and its last
 
     const int64_t qrs = (int64_t)p.Hq * D;   // elements between positions (Q, O)
     const int64_t krs = (int64_t)p.Hkv * D;  // elements between positions (K, V)
-    const int64_t bpos = (int64_t)b * p.nL + sub;
+    const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;       // key element 0
+    const int64_t qbase = (int64_t)b * p.qrows + (int64_t)sub * p.qsub;  // query 0's Q row
     const bf16 *qg = static_cast<const bf16 *>(p.q);
     const bf16 *kg = static_cast<const bf16 *>(p.k);
     const bf16 *vg = static_cast<const bf16 *>(p.v);
@@ -81,7 +85,7 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
     // holds dims ks*16 + 8*hi .. +7 of this lane's query.
     bf16x8 qop[D / 16];
     {
-        const bf16 *qp = qg + (bpos + (int64_t)(qvalid ? myq : 0) * p.stride) * qrs + (int64_t)h * D;
+        const bf16 *qp = qg + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs + (int64_t)h * D;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
@@ -94,8 +98,8 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
     for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int kend = min(q0 + QB, p.Lsub);
-    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    const int kend = min((min(q0 + QB, p.Lq) - 1) * p.qmul + p.qadd + 1, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 * p.qmul + p.qadd - p.weff + 1) : 0;
     constexpr int CH = D / 8;  // 16-byte chunks per row
 
     for (int t0 = kbeg & ~(KT - 1); t0 < kend; t0 += KT) {
@@ -115,10 +119,10 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
         __syncthreads();
 
         // Skip tiles wholly outside this wave's causal / window band.
-        const bool active = (t0 <= qw0 + QW - 1) && (p.weff == 0 || t0 + KT - 1 > qw0 - p.weff);
+        const bool active = (t0 <= lim1) && (p.weff == 0 || t0 + KT - 1 > lim0 - p.weff);
         if (!active) continue;
-        const bool need_mask = (t0 + KT - 1 > qw0) || (t0 + KT > p.Lsub) ||
-                               (p.weff != 0 && t0 <= qw0 + QW - 1 - p.weff);
+        const bool need_mask = (t0 + KT - 1 > lim0) || (t0 + KT > p.Lsub) ||
+                               (p.weff != 0 && t0 <= lim1 - p.weff);
 
         // S^T = K Q^T for two 32-key blocks.
         f32x16 sacc[2];
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
                 float x = sacc[kb][r] * scale_log2;
                 if (need_mask) {
                     const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                    const bool vis = key <= mylim && key < p.Lsub && (p.weff == 0 || mylim - key < p.weff);
                     x = vis ? x : -INFINITY;
                 }
                 sacc[kb][r] = x;
@@ -190,8 +194,8 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
     const float l_tot = l_run + wave_xor32(l_run);
     if (qvalid) {
         const float inv = 1.f / l_tot;
-        const int64_t pos = bpos + (int64_t)myq * p.stride;
-        bf16 *op = static_cast<bf16 *>(p.o) + pos * qrs + (int64_t)h * D;
+        const int64_t qrow = qbase + (int64_t)myq * p.qstride;
+        bf16 *op = static_cast<bf16 *>(p.o) + qrow * qrs + (int64_t)h * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
                 *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * r4 + 4 * hi) = y;
             }
         if (p.lse != nullptr && hi == 0)
-            p.lse[((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL)] =
+            p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] =
                 m_run * kLn2 + __logf(l_tot);
     }
 }
@@ -252,18 +256,18 @@ struct D128State {
 
 template <typename Issue>
 __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&issue_next, bool has_next,
-                                          int t0, const FwdArgs &p, int qw0, int myq, int hi, int l32, int l16,
-                                          int g2, const bf16x8 (&qop)[8], float scale_log2, D128State &st) {
+                                          int t0, const FwdArgs &p, int lim0, int lim1, int mylim, int hi, int l32,
+                                          int l16, int g2, const bf16x8 (&qop)[8], float scale_log2,
+                                          D128State &st) {
     constexpr int D = 128;
     constexpr int TILE = KT * D * 2;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
     __syncthreads();                // ... and every wave's; the previous tile is fully consumed
     if (has_next) issue_next();
 
-    const bool active = (t0 <= qw0 + QW - 1) && (p.weff == 0 || t0 + KT - 1 > qw0 - p.weff);
+    const bool active = (t0 <= lim1) && (p.weff == 0 || t0 + KT - 1 > lim0 - p.weff);
     if (!active) return;
-    const bool need_mask = (t0 + KT - 1 > qw0) || (t0 + KT > p.Lsub) ||
-                           (p.weff != 0 && t0 <= qw0 + QW - 1 - p.weff);
+    const bool need_mask = (t0 + KT - 1 > lim0) || (t0 + KT > p.Lsub) || (p.weff != 0 && t0 <= lim1 - p.weff);
     const char *kbuf = cur;
     const char *vbuf = cur + TILE;
 
@@ -294,8 +298,8 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
     float mx = -INFINITY;
     if (need_mask) {
         // visible <=> lo <= key <= hi, checked as one unsigned compare
-        const int lo = p.weff ? myq - p.weff + 1 : 0;
-        const int hi_key = min(myq, p.Lsub - 1);
+        const int lo = p.weff ? mylim - p.weff + 1 : 0;
+        const int hi_key = min(mylim, p.Lsub - 1);
         const unsigned span = (unsigned)(hi_key - lo);
         const int base = t0 + 4 * hi - lo;
 #pragma unroll
@@ -388,17 +392,21 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const int h = kvh * g + hgrp * HG + hw;
     const int qw0 = q0 + tb * QW;
     const int myq = qw0 + l32;
-    const bool qvalid = myq < p.Lsub;
+    const bool qvalid = myq < p.Lq;
+    const int mylim = myq * p.qmul + p.qadd;            // last key this query may see
+    const int lim0 = qw0 * p.qmul + p.qadd;             // ... for the wave's first query
+    const int lim1 = (qw0 + QW - 1) * p.qmul + p.qadd;  // ... and its last
 
     const int64_t qrs = (int64_t)p.Hq * D;
     const int64_t krs = (int64_t)p.Hkv * D;
-    const int64_t bpos = (int64_t)b * p.nL + sub;
+    const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;              // key element 0
+    const int64_t qbase = (int64_t)b * p.qrows + (int64_t)sub * p.qsub;  // query 0's Q row
     const bf16 *qg = static_cast<const bf16 *>(p.q);
     const bf16 *kg = static_cast<const bf16 *>(p.k) + (int64_t)kvh * D;
     const bf16 *vg = static_cast<const bf16 *>(p.v) + (int64_t)kvh * D;
 
-    const int kend = min(q0 + QB, p.Lsub);
-    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    const int kend = min((min(q0 + QB, p.Lq) - 1) * p.qmul + p.qadd + 1, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 * p.qmul + p.qadd - p.weff + 1) : 0;
     const int tfirst = kbeg & ~(KT - 1);
     const int ntiles = (kend - tfirst + KT - 1) / KT;
 
@@ -439,7 +447,7 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
 
     bf16x8 qop[D / 16];
     {
-        const bf16 *qp = qg + (bpos + (int64_t)(qvalid ? myq : 0) * p.stride) * qrs + (int64_t)h * D;
+        const bf16 *qp = qg + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs + (int64_t)h * D;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
@@ -455,18 +463,18 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
 
     for (int it = 0; it < ntiles; it += 2) {
         const int t0 = tfirst + it * KT;
-        d128_tile(buf0, [&] { issue(t0 + KT, buf1); }, it + 1 < ntiles, t0, p, qw0, myq, hi, l32, l16, g2, qop,
-                  scale_log2, st);
+        d128_tile(buf0, [&] { issue(t0 + KT, buf1); }, it + 1 < ntiles, t0, p, lim0, lim1, mylim, hi, l32, l16, g2,
+                  qop, scale_log2, st);
         if (it + 1 < ntiles)
-            d128_tile(buf1, [&] { issue(t0 + 2 * KT, buf0); }, it + 2 < ntiles, t0 + KT, p, qw0, myq, hi, l32,
-                      l16, g2, qop, scale_log2, st);
+            d128_tile(buf1, [&] { issue(t0 + 2 * KT, buf0); }, it + 2 < ntiles, t0 + KT, p, lim0, lim1, mylim, hi,
+                      l32, l16, g2, qop, scale_log2, st);
     }
 
     const float l_tot = pair_sum(st.l_run);
     if (qvalid) {
         const float inv = 1.f / l_tot;
-        const int64_t pos = bpos + (int64_t)myq * p.stride;
-        bf16 *op = static_cast<bf16 *>(p.o) + pos * qrs + (int64_t)h * D;
+        const int64_t qrow = qbase + (int64_t)myq * p.qstride;
+        bf16 *op = static_cast<bf16 *>(p.o) + qrow * qrs + (int64_t)h * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -477,7 +485,8 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
                 *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * r4 + 4 * hi) = y;
             }
         if (p.lse != nullptr && hi == 0)
-            p.lse[((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL)] = st.m_run * kLn2 + __logf(l_tot);
+            p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] =
+                st.m_run * kLn2 + __logf(l_tot);
     }
 }
 
@@ -487,7 +496,7 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
     const int g = a.Hq / a.Hkv;
     const int HG = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
     const int TB = NWAVE / HG;
-    const int nqblk = (a.Lsub + QW * TB - 1) / (QW * TB);
+    const int nqblk = (a.Lq + QW * TB - 1) / (QW * TB);
     const int64_t grid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const float sl2 = a.scale * kLog2e;
@@ -506,7 +515,7 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
             }
             {
                 const int TB2 = D128_NW / HG;
-                const int nqblk2 = (a.Lsub + QW * TB2 - 1) / (QW * TB2);
+                const int nqblk2 = (a.Lq + QW * TB2 - 1) / (QW * TB2);
                 const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
                 if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
                 hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid2), dim3(64 * D128_NW), 0, st, a, HG,

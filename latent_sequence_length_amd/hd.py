@@ -39,6 +39,7 @@ def load():
     P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.hd_expand_embed.argtypes = [P, I, I, I, P, I64, I, I, P, P]
     lib.hd_sfa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.hd_sfa_fwd_final.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.hd_sfa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.hd_sfa_decode_workspace_bytes.restype = SZ
     lib.hd_sfa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
@@ -46,7 +47,8 @@ def load():
     lib.hd_sfa_bwd_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
-    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_decode, lib.hd_sfa_bwd, lib.hd_rope):
+    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_decode, lib.hd_sfa_bwd,
+              lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -133,6 +135,27 @@ def hd_sfa_fwd(q, k, v, o, n, mode, window=0, scale=0.0, lse=None):
     _check(load().hd_sfa_fwd(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lp,
                              B, nL // n, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt,
                              _stream(q)))
+    return o
+
+
+def hd_sfa_fwd_final(q, k, v, o, n, mode, window=0, scale=0.0, lse=None):
+    """Final-stream queries of a KV-mirror layer: q, o [B, L, Hq, d] hold the
+    rows of stream n-1 only; k, v [B, n*L, Hkv, d]; lse [B, Hq, L] if given."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if k.shape != (B, n * L, Hkv, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch among q [B, L, Hq, d], k/v [B, n*L, Hkv, d], o")
+    dt = _dtype_code(q)
+    for t, name in ((k, "k"), (v, "v"), (o, "o")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q's {q.dtype}")
+    lp = None
+    if lse is not None:
+        if lse.shape != (B, Hq, L):
+            raise ValueError(f"lse must be {(B, Hq, L)}")
+        lp = _dev(lse, "lse", torch.float32)
+    _check(load().hd_sfa_fwd_final(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lp,
+                                   B, L, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt, _stream(q)))
     return o
 
 
@@ -231,6 +254,16 @@ def sfa_fwd(q, k, v, n, mode, window=0, scale=0.0, return_lse=False):
         B, nL, Hq, _ = q.shape
         lse = torch.empty((B, Hq, nL), dtype=torch.float32, device=q.device)
     hd_sfa_fwd(q, k, v, o, n, mode, window, scale, lse)
+    return (o, lse) if return_lse else o
+
+
+def sfa_fwd_final(q, k, v, n, mode, window=0, scale=0.0, return_lse=False):
+    o = torch.empty_like(q)
+    lse = None
+    if return_lse:
+        B, L, Hq, _ = q.shape
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    hd_sfa_fwd_final(q, k, v, o, n, mode, window, scale, lse)
     return (o, lse) if return_lse else o
 
 

@@ -32,7 +32,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
         "hd_status_string", "hd_last_error", "hd_version"])
 
@@ -54,11 +54,11 @@ def test_status_strings(lib):
 FAKE = 0x10000  # aligned non-null address; never dereferenced (validation fails first)
 
 
-def fwd(lib, **kw):
+def fwd(lib, entry="hd_sfa_fwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, L=8, n=2, Hq=4, Hkv=2, d=64,
              mode=0, window=0, scale=0.0, dt=0, stream=None)
     a.update(kw)
-    return lib.hd_sfa_fwd(*a.values())
+    return getattr(lib, entry)(*a.values())
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,8 +71,9 @@ def fwd(lib, **kw):
     (dict(dt=7), hd.HD_ERR_UNSUPPORTED), (dict(mode=2), hd.HD_ERR_UNSUPPORTED),
     (dict(L=1 << 29, n=4), hd.HD_ERR_UNSUPPORTED),
 ])
-def test_fwd_validation(lib, kw, code):
-    assert fwd(lib, **kw) == code
+@pytest.mark.parametrize("entry", ["hd_sfa_fwd", "hd_sfa_fwd_final"])
+def test_fwd_validation(lib, kw, code, entry):
+    assert fwd(lib, entry, **kw) == code
     assert hd.last_error() != ""
 
 
