@@ -363,6 +363,9 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
     st.l_run += lsum;
 }
 
+// GQ: the query map is not the identity (qmul, qadd) != (1, 0); a full layer
+// runs the GQ = false instance, whose band tests are the plain p <= j ones.
+template <bool GQ>
 __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
                                                                   float scale_log2) {
     constexpr int D = 128;
@@ -393,9 +396,10 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const int qw0 = q0 + tb * QW;
     const int myq = qw0 + l32;
     const bool qvalid = myq < p.Lq;
-    const int mylim = myq * p.qmul + p.qadd;            // last key this query may see
-    const int lim0 = qw0 * p.qmul + p.qadd;             // ... for the wave's first query
-    const int lim1 = (qw0 + QW - 1) * p.qmul + p.qadd;  // ... and its last
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    const int mylim = myq * qmul + qadd;            // last key this query may see
+    const int lim0 = qw0 * qmul + qadd;             // ... for the wave's first query
+    const int lim1 = (qw0 + QW - 1) * qmul + qadd;  // ... and its last
 
     const int64_t qrs = (int64_t)p.Hq * D;
     const int64_t krs = (int64_t)p.Hkv * D;
@@ -405,8 +409,8 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const bf16 *kg = static_cast<const bf16 *>(p.k) + (int64_t)kvh * D;
     const bf16 *vg = static_cast<const bf16 *>(p.v) + (int64_t)kvh * D;
 
-    const int kend = min((min(q0 + QB, p.Lq) - 1) * p.qmul + p.qadd + 1, p.Lsub);
-    const int kbeg = p.weff ? max(0, q0 * p.qmul + p.qadd - p.weff + 1) : 0;
+    const int kend = min((min(q0 + QB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
     const int tfirst = kbeg & ~(KT - 1);
     const int ntiles = (kend - tfirst + KT - 1) / KT;
 
@@ -518,8 +522,12 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
                 const int nqblk2 = (a.Lq + QW * TB2 - 1) / (QW * TB2);
                 const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
                 if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
-                hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel, dim3((unsigned)grid2), dim3(64 * D128_NW), 0, st, a, HG,
-                                   TB2, nqblk2, sl2);
+                if (a.qmul != 1 || a.qadd != 0)
+                    hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel<true>, dim3((unsigned)grid2), dim3(64 * D128_NW), 0,
+                                       st, a, HG, TB2, nqblk2, sl2);
+                else
+                    hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel<false>, dim3((unsigned)grid2), dim3(64 * D128_NW), 0,
+                                       st, a, HG, TB2, nqblk2, sl2);
             }
             break;
         default:
