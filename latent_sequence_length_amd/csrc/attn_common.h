@@ -40,6 +40,12 @@ constexpr bf16x2 kOnes2 = {(bf16)1.0f, (bf16)1.0f};
 
 __device__ __forceinline__ int swz128(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 
+// Swizzle of V tiles read with ds_read_b64_tr_b16: a 32-lane group reads 4
+// consecutive rows x 4 consecutive 16-byte chunks; XOR-ing row r's chunk index
+// with 4*(r%4) + (r/4)%4 puts the four rows in four different 64-byte quarters
+// of the 256-byte bank window (and is a permutation over any 16 rows).
+__device__ __forceinline__ int swzv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

@@ -352,7 +352,7 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
                 for (int jh = 0; jh < 2; ++jh) {
                     const int row = kb * 32 + 16 * m2 + 8 * jh + 4 * hi + (l16 >> 2);
                     const int dim = db * 32 + 16 * g2 + 4 * (l16 & 3);
-                    const char *addr = vbuf + row * 256 + (((dim >> 3) ^ swz128(row)) << 4) + ((dim >> 2) & 1) * 8;
+                    const char *addr = vbuf + row * 256 + (((dim >> 3) ^ swzv(row)) << 4) + ((dim >> 2) & 1) * 8;
                     half[jh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4 *)(addr));
                 }
@@ -420,31 +420,38 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     // of the sub-sequence re-read its last row (finite data, masked later).
     const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
     constexpr int PER = 16 / D128_NW;  // 1 KB copies of K (and of V) per wave per tile
-    int lrow[PER], lchunk[PER];
+    int lrow[PER], lchunk[PER], lchunkv[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         lrow[i] = (wave * PER + i) * 4 + (lane >> 4);
         lchunk[i] = ((lane & 15) ^ swz128(lrow[i])) * 8;
+        lchunkv[i] = ((lane & 15) ^ swzv(lrow[i])) * 8;
     }
-    unsigned boff[PER];  // per-lane byte offsets within a tile (rows unclamped)
+    unsigned boff[PER], boffv[PER];  // per-lane byte offsets of K / V within a tile (rows unclamped)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) boff[i] = (unsigned)(lrow[i] * rstride + lchunk[i]) * 2u;
+    for (int i = 0; i < PER; ++i) {
+        boff[i] = (unsigned)(lrow[i] * rstride + lchunk[i]) * 2u;
+        boffv[i] = (unsigned)(lrow[i] * rstride + lchunkv[i]) * 2u;
+    }
     auto issue = [&](int t0, char *dst) {
         const int64_t tbase = (bpos + (int64_t)t0 * p.stride) * krs;
         const bf16 *kt = kg + tbase, *vt = vg + tbase;
         const int rmax = p.Lsub - 1 - t0;
-        unsigned bo[PER];
+        unsigned bo[PER], bv[PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) bo[i] = boff[i];
+        for (int i = 0; i < PER; ++i) { bo[i] = boff[i]; bv[i] = boffv[i]; }
         if (rmax < KT - 1) {  // tail tile: rows past the end re-read the last row
 #pragma unroll
-            for (int i = 0; i < PER; ++i) bo[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunk[i]) * 2u;
+            for (int i = 0; i < PER; ++i) {
+                bo[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunk[i]) * 2u;
+                bv[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunkv[i]) * 2u;
+            }
         }
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int s0 = (wave * PER + i) * 64;
             lds_dma16_s(kt, bo[i], lds_addr(dst + s0 * 16));
-            lds_dma16_s(vt, bo[i], lds_addr(dst + TILE + s0 * 16));
+            lds_dma16_s(vt, bv[i], lds_addr(dst + TILE + s0 * 16));
         }
     };
     if (ntiles > 0) issue(tfirst, buf0);
