@@ -64,6 +64,8 @@ def _configure(lib):
     lib.oracle_sfa_fwd.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
     lib.oracle_sfa_final_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, I64, P, P]
     lib.oracle_sfa_final.argtypes = [P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P]
+    lib.oracle_sfa_final_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P, P, I64, P, P,
+                                              I64, P, P]
     lib.oracle_sfa_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, I64, D, P]
     lib.oracle_decode_append.argtypes = [P, P, P, I, I, I, I, I, I64]
     lib.oracle_sfa_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P, P, I64, P, P, I64, P, P]
@@ -293,6 +295,51 @@ def sfa_bwd(q, k, v, dout, n, mode, window=0, scale=0.0):
     dq, dk, dv = sfa_bwd_rows(q, k, v, dout, n, mode, window, scale,
                               qrows=np.arange(B * nL * Hq), krows=np.arange(B * nL * Hkv))
     return dq.reshape(B, nL, Hq, d), dk.reshape(B, nL, Hkv, d), dv.reshape(B, nL, Hkv, d)
+
+
+def final_row_stats(qf, k, v, doutf, n, mode, window=0, scale=0.0):
+    """lse and D = dO . O of the final-stream rows, both [B, Hq, L] float64,
+    from the forward definition (``sfa_final``)."""
+    o, lse = sfa_final(qf, k, v, n, mode, window, scale)
+    db, _ = _buf(doutf)
+    dbl = db.astype(np.float64) if db.dtype == np.float32 else _bf16_to_f64(db)
+    D = np.einsum("biHc,biHc->bHi", dbl, o)
+    return np.ascontiguousarray(lse), np.ascontiguousarray(D)
+
+
+def sfa_final_bwd_rows(qf, k, v, doutf, n, mode, window=0, scale=0.0, qrows=None, krows=None, stats=None):
+    """Gradients of sum(dOf * Of) for the final-stream queries: dq for flat
+    rows (b*L+i)*Hq+h of qf, dk / dv for flat key rows (b*nL+t)*Hkv+hk
+    (float64 [rows, d]).  stats = (lse, D) from ``final_row_stats``."""
+    qb, kb, vb, dt, B, L, Hq, Hkv, d = _final_shapes(qf, k, v, n)
+    db, dt2 = _buf(doutf)
+    if dt != dt2 or db.shape != qb.shape:
+        raise TypeError("doutf must match qf in shape and dtype")
+    if stats is None:
+        stats = final_row_stats(qf, k, v, doutf, n, mode, window, scale)
+    lse, D = (np.ascontiguousarray(x, dtype=np.float64) for x in stats)
+    qrows = np.ascontiguousarray(np.asarray([] if qrows is None else qrows, dtype=np.int64))
+    krows = np.ascontiguousarray(np.asarray([] if krows is None else krows, dtype=np.int64))
+    dq = np.empty((qrows.size, d))
+    dk = np.empty((krows.size, d))
+    dv = np.empty((krows.size, d))
+    rc = _load().oracle_sfa_final_bwd_rows(_p(qb), _p(kb), _p(vb), _p(db), dt, B, L, n, Hq, Hkv, d,
+                                           int(mode), int(window), float(scale), _p(lse), _p(D),
+                                           _p(qrows), qrows.size, _p(dq), _p(krows), krows.size,
+                                           _p(dk), _p(dv))
+    if rc:
+        raise ValueError("oracle_sfa_final_bwd_rows rejected its arguments")
+    return dq, dk, dv
+
+
+def sfa_final_bwd(qf, k, v, doutf, n, mode, window=0, scale=0.0):
+    """Full backward of the final-stream queries: dq [B, L, Hq, d], dk / dv
+    [B, nL, Hkv, d] (float64)."""
+    B, L, Hq, d = tuple(qf.shape)
+    nL, Hkv = tuple(k.shape)[1], tuple(k.shape)[2]
+    dq, dk, dv = sfa_final_bwd_rows(qf, k, v, doutf, n, mode, window, scale,
+                                    qrows=np.arange(B * L * Hq), krows=np.arange(B * nL * Hkv))
+    return dq.reshape(B, L, Hq, d), dk.reshape(B, nL, Hkv, d), dv.reshape(B, nL, Hkv, d)
 
 
 def rope(x, theta=10000.0, pos_base=None, pos_mul=0):

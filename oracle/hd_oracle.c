@@ -424,6 +424,83 @@ int oracle_sfa_bwd_rows(const void *q, const void *k, const void *v, const void 
 }
 
 /* ---------------------------------------------------------------------------
+ * Backward of the final-stream queries (oracle_sfa_final): the gradient of
+ * sum dOf * Of with respect to qf, k and v.  The same chain rule as above,
+ * with the query rows restricted to the final stream: query i sits at
+ * t = i*n + (n-1); a key row receives gradient only from the final-stream
+ * queries that see it (every expanded position's K/V, of every stream, can).
+ *
+ * lse and Drow are [B][Hq][L] (double) for the final rows.  qrows index qf
+ * ((b*L + i)*Hq + h) for dq [nq][d]; krows index k ((b*nL + t)*Hkv + hk) for
+ * dk, dv [nk][d].  Returns 0 or -1.
+ * ------------------------------------------------------------------------- */
+int oracle_sfa_final_bwd_rows(const void *qf, const void *k, const void *v, const void *doutf, int dtype,
+                              int B, int L, int n, int Hq, int Hkv, int d, int mode, int64_t W,
+                              double scale, const double *lse, const double *Drow,
+                              const int64_t *qrows, int64_t nq, double *dq,
+                              const int64_t *krows, int64_t nk, double *dk, double *dv) {
+    if (B < 1 || L < 1 || n < 1 || Hq < 1 || Hkv < 1 || d < 1 || Hq % Hkv) return -1;
+    if (W < 0 || (mode != OR_INTRA && mode != OR_CROSS)) return -1;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)d);
+    const int64_t nL = (int64_t)n * L;
+    const int g = Hq / Hkv;
+    int bad = 0;
+    /* dq of final-stream rows */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t r = 0; r < nq; ++r) {
+        int64_t id = qrows[r];
+        if (id < 0 || id >= (int64_t)B * L * Hq) { bad = 1; continue; }
+        int64_t h = id % Hq, i = (id / Hq) % L, b = id / Hq / L, kvh = h / g;
+        int64_t tq = i * n + (n - 1);
+        double lse_i = lse[(b * Hq + h) * L + i], D_i = Drow[(b * Hq + h) * L + i];
+        double *gq = dq + r * d;
+        for (int c = 0; c < d; ++c) gq[c] = 0.0;
+        for (int64_t tk = 0; tk <= tq; ++tk) {
+            if (!oracle_visible(tq, tk, n, mode, W)) continue;
+            int64_t koff = ((b * nL + tk) * Hkv + kvh) * d;
+            double s = 0.0, dp = 0.0;
+            for (int c = 0; c < d; ++c) {
+                s += load_elem(qf, dtype, id * d + c) * load_elem(k, dtype, koff + c);
+                dp += load_elem(doutf, dtype, id * d + c) * load_elem(v, dtype, koff + c);
+            }
+            double p = exp(scale * s - lse_i);
+            double ds = p * (dp - D_i);
+            for (int c = 0; c < d; ++c) gq[c] += scale * ds * load_elem(k, dtype, koff + c);
+        }
+    }
+    /* dk, dv of every key row, from the final-stream queries that see it */
+#pragma omp parallel for schedule(dynamic, 8)
+    for (int64_t r = 0; r < nk; ++r) {
+        int64_t id = krows[r];
+        if (id < 0 || id >= (int64_t)B * nL * Hkv) { bad = 1; continue; }
+        int64_t kvh = id % Hkv, tk = (id / Hkv) % nL, b = id / Hkv / nL;
+        double *gk = dk + r * d, *gv = dv + r * d;
+        for (int c = 0; c < d; ++c) gk[c] = gv[c] = 0.0;
+        for (int hh = 0; hh < g; ++hh) {
+            int64_t h = kvh * g + hh;
+            for (int64_t i = 0; i < L; ++i) {
+                int64_t tq = i * n + (n - 1);
+                if (tq < tk || !oracle_visible(tq, tk, n, mode, W)) continue;
+                int64_t qoff = ((b * L + i) * Hq + h) * d;
+                double lse_i = lse[(b * Hq + h) * L + i], D_i = Drow[(b * Hq + h) * L + i];
+                double s = 0.0, dp = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    s += load_elem(qf, dtype, qoff + c) * load_elem(k, dtype, id * d + c);
+                    dp += load_elem(doutf, dtype, qoff + c) * load_elem(v, dtype, id * d + c);
+                }
+                double p = exp(scale * s - lse_i);
+                double ds = p * (dp - D_i);
+                for (int c = 0; c < d; ++c) {
+                    gk[c] += scale * ds * load_elem(qf, dtype, qoff + c);
+                    gv[c] += p * load_elem(doutf, dtype, qoff + c);
+                }
+            }
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+/* ---------------------------------------------------------------------------
  * Rotary position embedding at the expanded positions.  "Hidden Decoding at
  * Scale", "Multi-Stream Expansion and Training Objective": the expanded
  * sequence S_1 .. S_nL is fed to the Transformer with contiguous RoPE

@@ -72,6 +72,15 @@ MUTANTS = [
       lambda o: pins.test_final_equals_full_layer_last_stream_rows(o, CROSS, 2)]),
     ("final lse stored query-major", "lse[(b * Hq + h) * L + i] = lrow[r];", "lse[(b * L + i) * Hq + h] = lrow[r];",
      [lambda o: pins.test_final_matches_sdpa_with_onebased_rows(o, INTRA, 2)]),
+    ("final bwd dq stops before the token's other streams", "for (int64_t tk = 0; tk <= tq; ++tk) {",
+     "for (int64_t tk = 0; tk <= i * n; ++tk) {",
+     [lambda o: pins.test_final_bwd_matches_autograd(o, CROSS, 0, 2)]),
+    ("final bwd keys skip the query of their own token", "if (tq < tk || !oracle_visible(tq, tk, n, mode, W)) continue;",
+     "if (tq <= tk || !oracle_visible(tq, tk, n, mode, W)) continue;",
+     [lambda o: pins.test_final_bwd_matches_autograd(o, INTRA, 0, 1), lambda o: pins.test_final_bwd_invariants(o, INTRA, 0)]),
+    ("final bwd D read from the lse slot", "double lse_i = lse[(b * Hq + h) * L + i], D_i = Drow[(b * Hq + h) * L + i];\n        double *gq",
+     "double lse_i = lse[(b * Hq + h) * L + i], D_i = lse[(b * Hq + h) * L + i];\n        double *gq",
+     [lambda o: pins.test_final_bwd_matches_autograd(o, CROSS, 2, 3)]),
 ]
 
 

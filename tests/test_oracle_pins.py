@@ -622,3 +622,90 @@ def test_final_rows_subset_matches_full(oracle):
     so, sl = oracle.sfa_final_rows(qf, k, v, n, CROSS, 2, rows=rows)
     np.testing.assert_array_equal(so, o.reshape(-1, d)[rows])
     np.testing.assert_array_equal(sl, lse.transpose(0, 2, 1).reshape(-1)[rows])
+
+
+def _final_bwd_inputs(B, L, n, Hq, Hkv, d, seed=80):
+    qf, k, v = _final_inputs(B, L, n, Hq, Hkv, d, seed)
+    dof = _rand((B, L, Hq, d), seed + 3)
+    return qf, k, v, dof
+
+
+def autograd_final_bwd(qf, k, v, dof, n, mode, W, scale=None):
+    """torch float64 autograd of SDPA with the rectangular mask made of the
+    1-based Figure 2 mask's rows t = i*n (GQA by repeating K/V)."""
+    L = qf.shape[1]
+    m = torch.from_numpy(brute.mask(n, L, mode, W)[np.arange(1, L + 1) * n - 1])
+    q64, k64, v64 = (x.double().requires_grad_(True) for x in (qf, k, v))
+    out = sdpa64(q64, k64, v64, attn_mask=m, scale=scale)
+    (out * dof.double()).sum().backward()
+    return q64.grad.numpy(), k64.grad.numpy(), v64.grad.numpy()
+
+
+@pytest.mark.parametrize("mode,W,g", [(INTRA, 0, 1), (CROSS, 0, 2), (INTRA, 3, 2), (CROSS, 2, 3), (CROSS, 1, 1)])
+def test_final_bwd_matches_autograd(oracle, mode, W, g):
+    B, L, n, Hkv, d = 2, 6, 3, 2, 8
+    qf, k, v, dof = _final_bwd_inputs(B, L, n, g * Hkv, Hkv, d, seed=81 + W + g)
+    dq, dk, dv = oracle.sfa_final_bwd(qf, k, v, dof, n, mode, W)
+    wq, wk, wv = autograd_final_bwd(qf, k, v, dof, n, mode, W)
+    for got, want in ((dq, wq), (dk, wk), (dv, wv)):
+        np.testing.assert_allclose(got, want, rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (CROSS, 2)])
+def test_final_bwd_equals_full_bwd_with_other_streams_silent(oracle, mode, W):
+    """The full layer's backward with dO = 0 on every non-final row gives the
+    same dK, dV, the final rows' dQ, and dQ = 0 elsewhere."""
+    B, L, n, Hq, Hkv, d = 1, 5, 3, 4, 2, 8
+    qf, k, v, dof = _final_bwd_inputs(B, L, n, Hq, Hkv, d, seed=90)
+    q = _rand((B, n * L, Hq, d), 93)
+    q[:, n - 1::n] = qf
+    do = torch.zeros((B, n * L, Hq, d))
+    do[:, n - 1::n] = dof
+    fq, fk, fv = oracle.sfa_bwd(q, k, v, do, n, mode, W)
+    dq, dk, dv = oracle.sfa_final_bwd(qf, k, v, dof, n, mode, W)
+    np.testing.assert_allclose(dk, fk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv, fv, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dq, fq[:, n - 1::n], rtol=1e-12, atol=1e-13)
+    mask = np.ones(n * L, dtype=bool)
+    mask[n - 1::n] = False
+    assert np.abs(fq[:, mask]).max() == 0.0
+
+
+def test_final_bwd_finite_differences(oracle):
+    """Central differences of sum(dOf * Of) through the final-stream forward."""
+    B, L, n, Hq, Hkv, d = 1, 3, 2, 2, 1, 4
+    qf, k, v, dof = _final_bwd_inputs(B, L, n, Hq, Hkv, d, seed=95)
+    dq, dk, dv = oracle.sfa_final_bwd(qf, k, v, dof, n, CROSS, 0)
+    h = 2.0 ** -12
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.sfa_final(qq, kk, vv, n, CROSS)
+        return float((o * dof.double().numpy()).sum())
+
+    rng = np.random.default_rng(4)
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        base = [qf, k, v]
+        for _ in range(6):
+            idx = tuple(int(rng.integers(s)) for s in base[which].shape)
+            plus = [x.clone() for x in base]
+            minus = [x.clone() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            fd = (loss(*plus) - loss(*minus)) / (2 * h)
+            assert abs(fd - grad[idx]) <= 2e-5 * max(1.0, abs(grad[idx])), (which, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (CROSS, 3)])
+def test_final_bwd_invariants(oracle, mode, W):
+    """Per (b, kv head): sum over all key rows of dK is 0 (each query's dS
+    sums to 0) and of dV is the sum of dOf over the group's heads and rows."""
+    B, L, n, Hq, Hkv, d = 2, 7, 4, 4, 2, 8
+    qf, k, v, dof = _final_bwd_inputs(B, L, n, Hq, Hkv, d, seed=97)
+    _, dk, dv = oracle.sfa_final_bwd(qf, k, v, dof, n, mode, W)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-12
+    want = dof.double().numpy().reshape(B, L, Hkv, Hq // Hkv, d).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), want, rtol=1e-12, atol=1e-12)
+    if mode == INTRA:   # keys of streams 0..n-2 get nothing in an intra layer
+        keep = np.zeros(n * L, dtype=bool)
+        keep[n - 1::n] = True
+        assert np.abs(dk[:, ~keep]).max() == 0.0 and np.abs(dv[:, ~keep]).max() == 0.0
