@@ -221,6 +221,23 @@ def main():
 
     if want("bwd_intra_n4"):
         comps["bwd_intra_n4"] = backward(I)
+    if want("bwd_final_cross_n4"):
+        # backward of the final-stream queries of the cross layer (KV-mirror
+        # training): dq of the 4096 final rows, dk/dv of all 16384 positions
+        cfg = X
+        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+        qf = q[:, cfg.n - 1::cfg.n].contiguous()
+        del q
+        dof = synth.normal(qf.shape, 9, cfg.dtype, dev)
+        of, lsef = hd.sfa_fwd_final(qf, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
+        dqf, dkf, dvf = torch.empty_like(qf), torch.empty_like(k), torch.empty_like(v)
+        wsf = torch.empty(hd.hd_sfa_bwd_final_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
+                          dtype=torch.uint8, device=dev)
+        fl = 2.5 * useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+        by = 2 * (4 * qf.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.L
+        comps["bwd_final_cross_n4"] = (
+            lambda: hd.hd_sfa_bwd_final(qf, k, v, of, dof, lsef, dqf, dkf, dvf, cfg.n, cfg.mode, cfg.window,
+                                        workspace=wsf), fl, by)
     if want("rope_qk"):
         # rotary embedding of the headline layer's q and k at the expanded
         # positions (in place); bytes = read + write of q and k

@@ -162,6 +162,29 @@ hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device workspace hd_sfa_bwd_final needs (0 if the sizes are
+ * invalid): one float32 per final-stream query row, B*Hq*L*4.
+ */
+size_t hd_sfa_bwd_final_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt);
+
+/*
+ * Backward of hd_sfa_fwd_final (training through a KV-mirror layer, where only
+ * the final stream is run; "Persistent KV and the KV-mirror Saving"): the
+ * gradients of sum(dout * o) over the final-stream rows with respect to q (the
+ * final rows), k and v (every position, of every stream: a key row receives
+ * gradient from the final-stream queries that see it, zero if none does).
+ * Same formulas as hd_sfa_bwd, with
+ *   q, o, dout, dq  [B][L][Hq][d]      k, v, dk, dv  [B][n*L][Hkv][d]  (dtype dt)
+ *   lse        float32 [B][Hq][L] as written by hd_sfa_fwd_final for these inputs
+ *   workspace  device memory of at least hd_sfa_bwd_final_workspace_bytes bytes
+ * Same requirements and errors as hd_sfa_bwd.
+ */
+hd_status hd_sfa_bwd_final(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                           const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq, int Hkv,
+                           int d, hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
  * Bytes of device workspace hd_sfa_decode needs for these sizes (0 if the
  * sizes are invalid).  The workspace holds float32 split-KV partial results.
  */

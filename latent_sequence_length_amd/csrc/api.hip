@@ -103,6 +103,40 @@ hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n, const void *c
     return device_status(hd::launch_expand_embed(a, static_cast<hipStream_t>(stream)), "expand_embed launch");
 }
 
+// Sub-sequence form and query map of one attention layer (FwdArgs, BwdArgs):
+// every position a query (final_only = false), or only the rows of stream
+// n-1, stored compactly, over K/V of every position (final_only = true).
+extern "C++" {
+template <typename A>
+static void layer_map(A &a, int L, int n, hd_mode mode, int window, bool final_only) {
+    a.nL = n * L;
+    const int64_t wx = (int64_t)n * window;  // cross window in positions
+    const int wcross = (window == 0 || wx >= (int64_t)n * L) ? 0 : (int)wx;
+    const int wintra = window >= L ? 0 : window;
+    if (!final_only) {
+        if (mode == HD_MODE_INTRA) { a.Lsub = L; a.nsub = n; a.stride = n; a.weff = wintra; }
+        else { a.Lsub = n * L; a.nsub = 1; a.stride = 1; a.weff = wcross; }
+        a.kbase = 0;
+        a.Lq = a.Lsub; a.qrows = n * L; a.qsub = 1; a.qstride = a.stride;  // Q rows laid out like K rows
+        a.qmul = 1; a.qadd = 0;
+        return;
+    }
+    a.nsub = 1;
+    a.Lq = L; a.qrows = L; a.qsub = 0; a.qstride = 1;  // query i is row i of the compact q
+    if (mode == HD_MODE_INTRA) {
+        // stream n-1's own sub-sequence: key j at position j*n + n-1
+        a.Lsub = L; a.stride = n; a.kbase = n - 1;
+        a.qmul = 1; a.qadd = 0;
+        a.weff = wintra;
+    } else {
+        // the whole expanded sequence; query i sits at position i*n + n-1
+        a.Lsub = n * L; a.stride = 1; a.kbase = 0;
+        a.qmul = n; a.qadd = n - 1;
+        a.weff = wcross;
+    }
+}
+}  // extern "C++"
+
 hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int L, int n,
                      int Hq, int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt, void *stream) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
@@ -116,21 +150,9 @@ hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float
         return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
     hd::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
-    if (mode == HD_MODE_INTRA) {
-        a.Lsub = L; a.nsub = n; a.stride = n;
-        a.weff = window;
-    } else {
-        a.Lsub = n * L; a.nsub = 1; a.stride = 1;
-        const int64_t w = (int64_t)n * window;
-        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
-    }
-    if (mode == HD_MODE_INTRA && window >= L) a.weff = 0;  // window covers everything
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    layer_map(a, L, n, mode, window, false);
     a.scale = resolve_scale(scale, d);
-    // every position is a query, its Q row laid out like its K row
-    a.kbase = 0;
-    a.Lq = a.Lsub; a.qrows = n * L; a.qsub = 1; a.qstride = a.stride;
-    a.qmul = 1; a.qadd = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
     return device_status(e, "sfa_fwd launch");
@@ -150,21 +172,8 @@ hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o,
         return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
     hd::FwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
-    a.nsub = 1;
-    a.Lq = L; a.qrows = L; a.qsub = 0; a.qstride = 1;  // query i is row i of the compact q
-    if (mode == HD_MODE_INTRA) {
-        // stream n-1's own sub-sequence: key j at position j*n + n-1
-        a.Lsub = L; a.stride = n; a.kbase = n - 1;
-        a.qmul = 1; a.qadd = 0;
-        a.weff = (window >= L) ? 0 : window;
-    } else {
-        // the whole expanded sequence; query i sits at position i*n + n-1
-        a.Lsub = n * L; a.stride = 1; a.kbase = 0;
-        a.qmul = n; a.qadd = n - 1;
-        const int64_t w = (int64_t)n * window;
-        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
-    }
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    layer_map(a, L, n, mode, window, true);
     a.scale = resolve_scale(scale, d);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
@@ -196,10 +205,10 @@ size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, h
     return hd::bwd_workspace_bytes(B, n * L, Hq);
 }
 
-hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
-                     const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq, int Hkv, int d,
-                     hd_mode mode, int window, float scale, hd_dtype dt, void *workspace, size_t workspace_bytes,
-                     void *stream) {
+static hd_status sfa_bwd_common(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                                const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq,
+                                int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                                size_t workspace_bytes, void *stream, bool final_only) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
     HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
     if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
@@ -213,25 +222,40 @@ hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o,
     HD_TRY(check_ptr(dv, "dv"));
     HD_TRY(check_ptr(lse, "lse"));
     HD_TRY(check_ptr(workspace, "workspace"));
-    const size_t need = hd::bwd_workspace_bytes(B, n * L, Hq);
+    const size_t need = hd::bwd_workspace_bytes(B, final_only ? L : n * L, Hq);
     if (workspace_bytes < need)
         return fail(HD_ERR_INVALID, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     hd::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
     a.dq = dq; a.dk = dk; a.dv = dv; a.drow = static_cast<float *>(workspace);
-    a.B = B; a.nL = n * L; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
-    if (mode == HD_MODE_INTRA) {
-        a.Lsub = L; a.nsub = n; a.stride = n;
-        a.weff = window >= L ? 0 : window;
-    } else {
-        a.Lsub = n * L; a.nsub = 1; a.stride = 1;
-        const int64_t w = (int64_t)n * window;
-        a.weff = (window == 0 || w >= (int64_t)n * L) ? 0 : (int)w;
-    }
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    layer_map(a, L, n, mode, window, final_only);
     a.scale = resolve_scale(scale, d);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_bwd_bf16(a, st) : hd::launch_sfa_bwd_f32(a, st);
-    return device_status(e, "sfa_bwd launch");
+    return device_status(e, final_only ? "sfa_bwd_final launch" : "sfa_bwd launch");
+}
+
+hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                     const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq, int Hkv, int d,
+                     hd_mode mode, int window, float scale, hd_dtype dt, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    return sfa_bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, L, n, Hq, Hkv, d, mode, window, scale, dt,
+                          workspace, workspace_bytes, stream, false);
+}
+
+size_t hd_sfa_bwd_final_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
+    if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
+    if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;
+    return hd::bwd_workspace_bytes(B, L, Hq);
+}
+
+hd_status hd_sfa_bwd_final(const void *q, const void *k, const void *v, const void *o, const void *dout,
+                           const float *lse, void *dq, void *dk, void *dv, int B, int L, int n, int Hq, int Hkv,
+                           int d, hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    return sfa_bwd_common(q, k, v, o, dout, lse, dq, dk, dv, B, L, n, Hq, Hkv, d, mode, window, scale, dt,
+                          workspace, workspace_bytes, stream, true);
 }
 
 size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap) {

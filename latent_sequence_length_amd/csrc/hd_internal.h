@@ -64,16 +64,19 @@ hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
 // Backward of the prefill, in the same sub-sequence form as FwdArgs.
+// The query side follows the same map as FwdArgs (full layer: identity;
+// final-stream queries of a KV-mirror layer: compact rows, lim(p) = p*qmul + qadd).
 struct BwdArgs {
-    const void *q, *k, *v, *o, *dout;
-    const float *lse;  // [B][Hq][nL], natural log, from the forward
+    const void *q, *k, *v, *o, *dout;  // q, o, dout [B][qrows][Hq][d]
+    const float *lse;  // [B][Hq][qrows], natural log, from the forward
     void *dq, *dk, *dv;
-    float *drow;       // workspace [B][Hq][nL]: D = dO . O per query row
+    float *drow;       // workspace [B][Hq][qrows]: D = dO . O per query row
     int B, nL, Hq, Hkv, d;
-    int Lsub, nsub, stride, weff;
+    int Lsub, nsub, stride, kbase, weff;
     float scale;
+    int Lq, qrows, qsub, qstride, qmul, qadd;
 };
-size_t bwd_workspace_bytes(int B, int nL, int Hq);
+size_t bwd_workspace_bytes(int B, int qrows, int Hq);
 hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st);
 

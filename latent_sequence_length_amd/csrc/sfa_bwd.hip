@@ -36,9 +36,9 @@ constexpr int BKW = 128;  // keys per workgroup (dK/dV kernel)
 // 1. D = dO . O per query row; 16 lanes per row, fp32.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_drow_kernel(BwdArgs p) {
-    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b*nL + t)*Hq + h
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b*qrows + t)*Hq + h
     const int part = threadIdx.x & 15;
-    const int64_t nrows = (int64_t)p.B * p.nL * p.Hq;
+    const int64_t nrows = (int64_t)p.B * p.qrows * p.Hq;
     constexpr int PER = D / 16;
     float acc = 0.f;
     if (row < nrows) {
@@ -50,19 +50,36 @@ __global__ __launch_bounds__(256) void bwd_drow_kernel(BwdArgs p) {
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
     if (row < nrows && part == 0) {
-        const int64_t h = row % p.Hq, t = (row / p.Hq) % p.nL, b = row / p.Hq / p.nL;
-        p.drow[(b * p.Hq + h) * p.nL + t] = acc;
+        const int64_t h = row % p.Hq, t = (row / p.Hq) % p.qrows, b = row / p.Hq / p.qrows;
+        p.drow[(b * p.Hq + h) * p.qrows + t] = acc;
     }
 }
 
-// Row (b, sub, j) of the sub-sequence form -> expanded position.
+// Key element j of sub-sequence (b, sub) -> K/V row (expanded position).
 __device__ __forceinline__ int64_t sub_pos(const BwdArgs &p, int b, int sub, int j) {
-    return (int64_t)b * p.nL + sub + (int64_t)j * p.stride;
+    return (int64_t)b * p.nL + p.kbase + sub + (int64_t)j * p.stride;
 }
 
-// Index of a query row's lse / D entry: [b][h][position within the batch row].
-__device__ __forceinline__ int64_t row_stat(const BwdArgs &p, int b, int h, int64_t pos) {
-    return ((int64_t)b * p.Hq + h) * p.nL + (pos - (int64_t)b * p.nL);
+// Query i of sub-sequence (b, sub) -> Q / O / dO row.
+__device__ __forceinline__ int64_t q_row(const BwdArgs &p, int b, int sub, int i) {
+    return (int64_t)b * p.qrows + (int64_t)sub * p.qsub + (int64_t)i * p.qstride;
+}
+
+// Index of a query row's lse / D entry: [b][h][row within the batch row].
+__device__ __forceinline__ int64_t row_stat(const BwdArgs &p, int b, int h, int64_t qrow) {
+    return ((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows);
+}
+
+// First query whose band reaches key element j (lim(i) >= j), or 0.
+__device__ __forceinline__ int first_query(const BwdArgs &p, int j) {
+    return j <= p.qadd ? 0 : (j - p.qadd + p.qmul - 1) / p.qmul;
+}
+
+// One past the last query whose window still holds key element j (Lq without a window).
+__device__ __forceinline__ int query_end(const BwdArgs &p, int j) {
+    if (p.weff == 0) return p.Lq;
+    const int num = j + p.weff - 1 - p.qadd;  // lim(i) <= num
+    return num < 0 ? 0 : min(p.Lq, num / p.qmul + 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -70,15 +87,15 @@ __device__ __forceinline__ int64_t row_stat(const BwdArgs &p, int b, int h, int6
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs p) {
     const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, sub, i, h)
-    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lsub * p.Hq;
+    const int64_t nrows = (int64_t)p.B * p.nsub * p.Lq * p.Hq;
     if (row >= nrows) return;
     const int h = (int)(row % p.Hq);
     int64_t r = row / p.Hq;
-    const int i = (int)(r % p.Lsub); r /= p.Lsub;
+    const int i = (int)(r % p.Lq); r /= p.Lq;
     const int sub = (int)(r % p.nsub);
     const int b = (int)(r / p.nsub);
     const int kvh = h / (p.Hq / p.Hkv);
-    const int64_t pos = sub_pos(p, b, sub, i);
+    const int64_t pos = q_row(p, b, sub, i);
     const float *qp = static_cast<const float *>(p.q) + (pos * p.Hq + h) * D;
     const float *gp = static_cast<const float *>(p.dout) + (pos * p.Hq + h) * D;
     const float *kg = static_cast<const float *>(p.k);
@@ -87,8 +104,9 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdArgs p) {
 #pragma unroll
     for (int c = 0; c < D; ++c) { qv[c] = qp[c]; gv[c] = gp[c]; acc[c] = 0.f; }
     const float lse = p.lse[row_stat(p, b, h, pos)], Dr = p.drow[row_stat(p, b, h, pos)];
-    const int jbeg = p.weff ? max(0, i - p.weff + 1) : 0;
-    for (int j = jbeg; j <= i; ++j) {
+    const int lim = i * p.qmul + p.qadd;  // last visible key element
+    const int jbeg = p.weff ? max(0, lim - p.weff + 1) : 0;
+    for (int j = jbeg; j <= lim; ++j) {
         const int64_t off = (sub_pos(p, b, sub, j) * p.Hkv + kvh) * D;
         float s = 0.f, dp = 0.f;
 #pragma unroll
@@ -125,11 +143,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(BwdArgs p) {
     float ak[D], av[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) ak[c] = av[c] = 0.f;
-    const int iend = p.weff ? min(p.Lsub - 1, j + p.weff - 1) : p.Lsub - 1;
+    const int ibeg = first_query(p, j), iend = query_end(p, j);
     for (int hh = 0; hh < g; ++hh) {
         const int h = kvh * g + hh;
-        for (int i = j; i <= iend; ++i) {
-            const int64_t qpos = sub_pos(p, b, sub, i);
+        for (int i = ibeg; i < iend; ++i) {
+            const int64_t qpos = q_row(p, b, sub, i);
             const float *qp = static_cast<const float *>(p.q) + (qpos * p.Hq + h) * D;
             const float *gp = static_cast<const float *>(p.dout) + (qpos * p.Hq + h) * D;
             float s = 0.f, dp = 0.f;
@@ -218,8 +236,9 @@ __device__ __forceinline__ void store_rows(bf16 *out, const f32x16 (&acc)[D / 32
 //   S = Q K^T, dP = dO V^T      [32 q x 32 k]: lane = key, registers = queries
 //   P = exp(S*scale - lse), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS   [D x 32 k]
-template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nkblk) {
+// GQ: the query map is not the identity (final-stream queries).
+template <int D, bool GQ>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     constexpr int PITCH = 2 * D + 16;
     constexpr int HS = 4;  // heads of the group staged per round
     __shared__ __attribute__((aligned(16))) char Qs[HS][BQT * PITCH];
@@ -262,33 +281,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
     for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
 
     const float c2 = p.scale * kLog2e;
-    // queries that see keys [j0, j0 + 128): i >= j0 and i - j < weff
-    const int iend = p.weff ? min(p.Lsub, j0 + BKW - 1 + p.weff) : p.Lsub;
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    // queries that see keys [j0, j0 + 128): lim(i) >= j0 and lim(i) - j < weff
+    const int ibeg = first_query(p, j0);
+    const int iend = query_end(p, min(j0 + BKW, p.Lsub) - 1);
     for (int h0 = 0; h0 < g; h0 += HS) {
         const int nh = min(HS, g - h0);
-        for (int i0 = j0; i0 < iend; i0 += BQT) {
+        for (int i0 = ibeg; i0 < iend; i0 += BQT) {
             __syncthreads();  // previous tiles consumed
-            const int nvalid = min(BQT, p.Lsub - i0);
-            const int64_t qpos0 = sub_pos(p, b, sub, i0);
+            const int nvalid = min(BQT, p.Lq - i0);
+            const int64_t qpos0 = q_row(p, b, sub, i0);
             for (int hh = 0; hh < nh; ++hh) {
                 const int h = kvh * g + h0 + hh;
                 stage_rows<D, BQT>(Qs[hh], static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D,
-                                   p.stride * qrs, nvalid);
+                                   p.qstride * qrs, nvalid);
                 stage_rows<D, BQT>(Gs[hh], static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D,
-                                   p.stride * qrs, nvalid);
+                                   p.qstride * qrs, nvalid);
             }
             if (tid < BQT * nh) {
                 const int hh = tid / BQT, r = tid % BQT;
-                const int64_t st = row_stat(p, b, kvh * g + h0 + hh, qpos0 + (int64_t)r * p.stride);
+                const int64_t st = row_stat(p, b, kvh * g + h0 + hh, qpos0 + (int64_t)min(r, nvalid - 1) * p.qstride);
                 Ls[hh][r] = r < nvalid ? p.lse[st] * kLog2e : 0.f;
                 Ds[hh][r] = r < nvalid ? p.drow[st] : 0.f;
             }
             __syncthreads();
 
-            const bool active = (i0 + BQT - 1 >= jw0) && (p.weff == 0 || i0 < jw0 + 31 + p.weff) && jw0 < p.Lsub;
+            const int lim_first = i0 * qmul + qadd, lim_last = (i0 + BQT - 1) * qmul + qadd;
+            const bool active = (lim_last >= jw0) && (p.weff == 0 || lim_first < jw0 + 31 + p.weff) && jw0 < p.Lsub;
             if (!active) continue;
-            const bool need_mask = (i0 < jw0 + 31) || (i0 + BQT > p.Lsub) || (jw0 + 32 > p.Lsub) ||
-                                   (p.weff != 0 && i0 + BQT - 1 - jw0 >= p.weff);
+            const bool need_mask = (lim_first < jw0 + 31) || (i0 + BQT > p.Lq) || (jw0 + 32 > p.Lsub) ||
+                                   (p.weff != 0 && lim_last - jw0 >= p.weff);
             for (int hh = 0; hh < nh; ++hh) {
                 const char *qs = Qs[hh], *gs = Gs[hh];
                 f32x16 s = f32x16{}, dp = f32x16{};
@@ -307,10 +329,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
                     for (int jj = 0; jj < 8; ++jj) {
                         const int r = 8 * m2 + jj;
                         const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
-                        const int i = i0 + qi;
+                        const int i = i0 + qi, li = i * qmul + qadd;
                         bool vis = true;
                         if (need_mask)
-                            vis = kvalid && i < p.Lsub && i >= myk && (p.weff == 0 || i - myk < p.weff);
+                            vis = kvalid && i < p.Lq && li >= myk && (p.weff == 0 || li - myk < p.weff);
                         const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -Ls[hh][qi]));
                         const float pr = vis ? e : 0.f;  // a select, not a branch
                         pop[m2][jj] = (bf16)pr;
@@ -337,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p, int nk
 // queries (HG*TB = 4), sharing 64-key K/V tiles; per tile:
 //   S^T = K Q^T, dP^T = V dO^T   [64 k x 32 q]: lane = query, registers = keys
 //   dS^T = P^T (dP^T - D);  dQ^T += K^T dS^T   [D x 32 q]
-template <int D>
+template <int D, bool GQ>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, int TB, int nqblk) {
     constexpr int PITCH = 2 * D + 16;
     __shared__ __attribute__((aligned(16))) char Ks[2][BKT * PITCH];  // two 64-key sub-tiles per round
@@ -361,9 +383,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
     const int h = kvh * g + hgrp * HG + wave % HG;
     const int qw0 = q0 + 32 * (wave / HG);
     const int myq = qw0 + l32;
-    const bool qvalid = myq < p.Lsub;
+    const bool qvalid = myq < p.Lq;
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    const int mylim = myq * qmul + qadd, lim0 = qw0 * qmul + qadd, lim1 = (qw0 + 31) * qmul + qadd;
     const int64_t qrs = (int64_t)p.Hq * D, krs = (int64_t)p.Hkv * D;
-    const int64_t pos = sub_pos(p, b, sub, qvalid ? myq : 0);
+    const int64_t pos = q_row(p, b, sub, qvalid ? myq : 0);
 
     // B operands Q^T and dO^T: lane = query, k-slots = dims 16*ks + 8*hi .. +7
     bf16x8 qf[D / 16], gf[D / 16];
@@ -383,8 +407,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
-    const int kend = min(q0 + 32 * TB, p.Lsub);
-    const int kbeg = p.weff ? max(0, q0 - p.weff + 1) : 0;
+    const int kend = min((min(q0 + 32 * TB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
     for (int tr = kbeg & ~(BKT - 1); tr < kend; tr += 2 * BKT) {
         __syncthreads();  // previous tiles consumed
 #pragma unroll
@@ -401,10 +425,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
         for (int u = 0; u < 2; ++u) {
             const int t0 = tr + u * BKT;
             const char *ks_ = Ks[u], *vs_ = Vs[u];
-            const bool active = (t0 < kend) && (t0 <= qw0 + 31) && (p.weff == 0 || t0 + BKT - 1 > qw0 - p.weff);
+            const bool active = (t0 < kend) && (t0 <= lim1) && (p.weff == 0 || t0 + BKT - 1 > lim0 - p.weff);
             if (!active) continue;
             const bool need_mask =
-                (t0 + BKT - 1 > qw0) || (t0 + BKT > p.Lsub) || (p.weff != 0 && t0 <= qw0 + 31 - p.weff);
+                (t0 + BKT - 1 > lim0) || (t0 + BKT > p.Lsub) || (p.weff != 0 && t0 <= lim1 - p.weff);
             f32x16 s[2], dp[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -427,7 +451,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
                         const int r = 8 * m2 + jj;
                         const int key = t0 + 32 * kb + 8 * (r >> 2) + 4 * hi + (r & 3);
                         bool vis = true;
-                        if (need_mask) vis = key <= myq && key < p.Lsub && (p.weff == 0 || myq - key < p.weff);
+                        if (need_mask) vis = key <= mylim && key < p.Lsub && (p.weff == 0 || mylim - key < p.weff);
                         const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2));
                         const float pr = vis ? e : 0.f;  // a select, not a branch
                         dsop[kb * 2 + m2][jj] = (bf16)(pr * (dp[kb][r] - Dq));
@@ -445,9 +469,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
     if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + pos * qrs + (int64_t)h * D, dq, p.scale, hi);
 }
 
+// dK and dV rows that no key sub-sequence covers (the other streams of a
+// final-stream intra layer: position t is covered iff (t - kbase) mod stride
+// < nsub) receive no gradient: write zeros, 16 bytes per thread.
+__global__ __launch_bounds__(256) void bwd_zero_uncovered_kernel(BwdArgs p, int chunks_per_row, int64_t nchunks) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= nchunks) return;
+    const int64_t t = (c / chunks_per_row / p.Hkv) % p.nL;  // position within the batch row
+    const int64_t rel = ((t - p.kbase) % p.stride + p.stride) % p.stride;
+    if (rel < p.nsub) return;
+    reinterpret_cast<uint4 *>(p.dk)[c] = uint4{0, 0, 0, 0};
+    reinterpret_cast<uint4 *>(p.dv)[c] = uint4{0, 0, 0, 0};
+}
+
+hipError_t launch_zero_uncovered(const BwdArgs &a, int elem_bytes, hipStream_t st) {
+    if (a.nsub == a.stride) return hipSuccess;  // every position is some sub-sequence's key
+    const int chunks_per_row = a.d * elem_bytes / 16;
+    const int64_t nchunks = (int64_t)a.B * a.nL * a.Hkv * chunks_per_row;
+    const int64_t grid = (nchunks + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_zero_uncovered_kernel, dim3((unsigned)grid), dim3(256), 0, st, a, chunks_per_row,
+                       nchunks);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_drow(const BwdArgs &a, hipStream_t st) {
-    const int64_t rows = (int64_t)a.B * a.nL * a.Hq;
+    const int64_t rows = (int64_t)a.B * a.qrows * a.Hq;
     const int64_t grid = (rows + 15) / 16;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     switch (a.d) {
@@ -459,26 +507,31 @@ hipError_t launch_drow(const BwdArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool GQ>
 hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
     const int g = a.Hq / a.Hkv;
     const int nkblk = (a.Lsub + BKW - 1) / BKW;
     const int64_t kgrid = (int64_t)nkblk * a.B * a.Hkv * a.nsub;
     const int HG = (g % 4 == 0) ? 4 : (g % 2 == 0) ? 2 : 1;
     const int TB = 4 / HG;
-    const int nqblk = (a.Lsub + 32 * TB - 1) / (32 * TB);
+    const int nqblk = (a.Lq + 32 * TB - 1) / (32 * TB);
     const int64_t qgrid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
     if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(bwd_dkdv_bf16_kernel<D>, dim3((unsigned)kgrid), dim3(256), 0, st, a, nkblk);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)kgrid), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_bf16_kernel<D>, dim3((unsigned)qgrid), dim3(256), 0, st, a, HG, TB, nqblk);
+    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GQ>), dim3((unsigned)qgrid), dim3(256), 0, st, a, HG, TB, nqblk);
     return hipGetLastError();
 }
 
 template <int D>
+hipError_t launch_bf16_map(const BwdArgs &a, hipStream_t st) {
+    return (a.qmul != 1 || a.qadd != 0) ? launch_bf16_d<D, true>(a, st) : launch_bf16_d<D, false>(a, st);
+}
+
+template <int D>
 hipError_t launch_f32_d(const BwdArgs &a, hipStream_t st) {
-    const int64_t qrows = (int64_t)a.B * a.nsub * a.Lsub * a.Hq;
+    const int64_t qrows = (int64_t)a.B * a.nsub * a.Lq * a.Hq;
     const int64_t krows = (int64_t)a.B * a.nsub * a.Lsub * a.Hkv;
     if ((qrows + 63) / 64 > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_dq_f32_kernel<D>, dim3((unsigned)((qrows + 63) / 64)), dim3(64), 0, st, a);
@@ -490,21 +543,25 @@ hipError_t launch_f32_d(const BwdArgs &a, hipStream_t st) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int nL, int Hq) { return (size_t)B * Hq * nL * sizeof(float); }
+size_t bwd_workspace_bytes(int B, int qrows, int Hq) { return (size_t)B * Hq * qrows * sizeof(float); }
 
 hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st) {
-    hipError_t e = launch_drow<bf16>(a, st);
+    hipError_t e = launch_zero_uncovered(a, 2, st);
+    if (e != hipSuccess) return e;
+    e = launch_drow<bf16>(a, st);
     if (e != hipSuccess) return e;
     switch (a.d) {
-        case 32: return launch_bf16_d<32>(a, st);
-        case 64: return launch_bf16_d<64>(a, st);
-        case 128: return launch_bf16_d<128>(a, st);
+        case 32: return launch_bf16_map<32>(a, st);
+        case 64: return launch_bf16_map<64>(a, st);
+        case 128: return launch_bf16_map<128>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st) {
-    hipError_t e = launch_drow<float>(a, st);
+    hipError_t e = launch_zero_uncovered(a, 4, st);
+    if (e != hipSuccess) return e;
+    e = launch_drow<float>(a, st);
     if (e != hipSuccess) return e;
     switch (a.d) {
         case 32: return launch_f32_d<32>(a, st);

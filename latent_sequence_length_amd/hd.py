@@ -46,9 +46,12 @@ def load():
     lib.hd_sfa_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.hd_sfa_bwd_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
+    lib.hd_sfa_bwd_final_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.hd_sfa_bwd_final_workspace_bytes.restype = SZ
+    lib.hd_sfa_bwd_final.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
     for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_decode, lib.hd_sfa_bwd,
-              lib.hd_rope):
+              lib.hd_sfa_bwd_final, lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -237,6 +240,35 @@ def hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window=0, scale=0.0, 
     return dq, dk, dv
 
 
+def hd_sfa_bwd_final_workspace_bytes(B, L, n, Hq, Hkv, d, dtype=torch.bfloat16):
+    return int(load().hd_sfa_bwd_final_workspace_bytes(B, L, n, Hq, Hkv, d, _DT[dtype]))
+
+
+def hd_sfa_bwd_final(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window=0, scale=0.0, workspace=None):
+    """Backward of the final-stream queries: q, o, dout, dq [B, L, Hq, d];
+    k, v, dk, dv [B, n*L, Hkv, d]; lse [B, Hq, L] from hd_sfa_fwd_final."""
+    B, L, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if (k.shape != (B, n * L, Hkv, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape
+            or dq.shape != q.shape or dk.shape != k.shape or dv.shape != k.shape):
+        raise ValueError("shape mismatch among q, k, v, o, dout, dq, dk, dv")
+    if lse.shape != (B, Hq, L):
+        raise ValueError(f"lse must be {(B, Hq, L)}")
+    dt = _dtype_code(q)
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q's {q.dtype}")
+    if workspace is None:
+        need = hd_sfa_bwd_final_workspace_bytes(B, L, n, Hq, Hkv, d, q.dtype)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(load().hd_sfa_bwd_final(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(dout, "dout"),
+                                   _dev(lse, "lse", torch.float32), _dev(dq, "dq"), _dev(dk, "dk"),
+                                   _dev(dv, "dv"), B, L, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt,
+                                   _dev(workspace, "workspace"), wbytes, _stream(q)))
+    return dq, dk, dv
+
+
 # --------------------------------------------------------------------------
 # Allocating conveniences.
 # --------------------------------------------------------------------------
@@ -275,6 +307,11 @@ def sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, sca
 def sfa_bwd(q, k, v, o, dout, lse, n, mode, window=0, scale=0.0):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     return hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window, scale)
+
+
+def sfa_bwd_final(q, k, v, o, dout, lse, n, mode, window=0, scale=0.0):
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    return hd_sfa_bwd_final(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window, scale)
 
 
 def rope(x, theta=10000.0, pos_base=None, pos_mul=0):

@@ -33,6 +33,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_sfa_bwd_final_workspace_bytes", "hd_sfa_bwd_final",
         "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
         "hd_status_string", "hd_last_error", "hd_version"])
 
@@ -106,12 +107,12 @@ def test_workspace_size_is_monotone_and_zero_on_bad_sizes(lib):
     assert a % (64 * 4 * 32 * 130 * 4) == 0
 
 
-def bwd(lib, **kw):
+def bwd(lib, entry="hd_sfa_bwd", **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE,
              B=1, L=8, n=2, Hq=4, Hkv=2, d=64, mode=0, window=0, scale=0.0, dt=0,
              workspace=FAKE, workspace_bytes=1 << 20, stream=None)
     a.update(kw)
-    return lib.hd_sfa_bwd(*a.values())
+    return getattr(lib, entry)(*a.values())
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -127,11 +128,26 @@ def test_bwd_validation(lib, kw, code):
     assert hd.last_error() != ""
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), hd.HD_ERR_INVALID), (dict(Hq=3), hd.HD_ERR_INVALID), (dict(dv=None), hd.HD_ERR_INVALID),
+    (dict(workspace_bytes=1 * 4 * 8 * 4 - 1), hd.HD_ERR_INVALID),   # B*Hq*L*4 = 128 bytes needed
+    (dict(d=16), hd.HD_ERR_UNSUPPORTED), (dict(mode=2), hd.HD_ERR_UNSUPPORTED),
+    (dict(L=1 << 29, n=4), hd.HD_ERR_UNSUPPORTED),
+])
+def test_bwd_final_validation(lib, kw, code):
+    assert bwd(lib, "hd_sfa_bwd_final", **kw) == code
+    assert hd.last_error() != ""
+
+
 def test_bwd_workspace_size(lib):
     f = hd.hd_sfa_bwd_workspace_bytes
     assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4
     assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4
     assert f(0, 8, 2, 4, 2, 64) == 0 and f(1, 8, 2, 4, 3, 64) == 0 and f(1, 8, 2, 4, 2, 96) == 0
+    ff = hd.hd_sfa_bwd_final_workspace_bytes
+    assert ff(1, 4096, 4, 32, 8, 128) == 4096 * 32 * 4
+    assert ff(2, 100, 3, 8, 2, 64) == 2 * 8 * 100 * 4
+    assert ff(0, 8, 2, 4, 2, 64) == 0 and ff(1, 8, 2, 4, 2, 96) == 0
 
 
 def test_rope_validation(lib):
