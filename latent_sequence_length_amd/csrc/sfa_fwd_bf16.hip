@@ -378,10 +378,24 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
     const int g = p.Hq / p.Hkv, ngrp = g / HG;
 
+    // Workgroup -> (query block, group).  Dispatch is round-robin over the 8
+    // XCDs (XCD bid % 8 runs its workgroups in bid order); the map keeps each
+    // XCD's share balanced (longest blocks first) and its groups few:
+    // whole groups per XCD when the group count is a multiple of 8, each
+    // group spread over 8/G XCDs when G divides 8, else round-robin.
     const int nrest = p.B * p.Hkv * ngrp * p.nsub;
     const int nwg = nrest * nqblk;
     const int bid = blockIdx.x;
-    const int lid = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+    int lid = bid;
+    if (nwg % 8 == 0) {
+        const int x = bid % 8, j = bid / 8;
+        if (nrest % 8 == 0) {
+            lid = x * (nwg / 8) + j;
+        } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
+            const int r = 8 / nrest;
+            lid = (x / r) * nqblk + j * r + x % r;
+        }
+    }
     const int qblk = nqblk - 1 - lid % nqblk;
     int rest = lid / nqblk;
     const int sub = rest % p.nsub; rest /= p.nsub;
