@@ -135,21 +135,29 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
                 sacc[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kr + ks * 16), qop[ks], sacc[kb]);
         }
 
-        // Scale to log2 units, mask, tile max.
+        // Scale to log2 units, mask (visible <=> lo <= key <= hi_key, one
+        // unsigned compare and a select per score), tile max.
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] *= scale_log2;
+        if (need_mask) {  // uniform: only tiles on the band edges
+            const int lo = p.weff ? mylim - p.weff + 1 : 0;
+            const unsigned span = (unsigned)(min(mylim, p.Lsub - 1) - lo);
+            const int base = t0 + 4 * hi - lo;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const unsigned u = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+                    sacc[kb][r] = (u <= span) ? sacc[kb][r] : -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = sacc[kb][r] * scale_log2;
-                if (need_mask) {
-                    const int key = t0 + kb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-                    const bool vis = key <= mylim && key < p.Lsub && (p.weff == 0 || mylim - key < p.weff);
-                    x = vis ? x : -INFINITY;
-                }
-                sacc[kb][r] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
         mx = fmaxf(mx, wave_xor32(mx));
         const float m_new = fmaxf(m_run, mx);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
