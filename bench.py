@@ -18,6 +18,7 @@ headline value is useful TFLOP/s of the intra-stream prefill (4*d*Hq FLOPs per
 visible query/key pair).  Prints one JSON line.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -57,6 +58,40 @@ def useful_flops_final(B, L, n, Hq, d, mode, window=0):
         return w * (w + 1) // 2 + (T - w) * w
     pairs = tri(L, window) * (n if mode == 1 else 1)
     return 4.0 * d * Hq * B * pairs
+
+
+def measured_peaks(dev):
+    """The machine's sustained rates, reported beside the published peaks:
+    an MFMA-only loop (libhd_probe.so, 8 independent bf16 32x32x16 chains
+    per wave, 4 waves per SIMD) and a 1 GiB device copy (read + write)."""
+    out = {}
+    path = os.path.join(ROOT, "latent_sequence_length_amd", "libhd_probe.so")
+    if os.path.exists(path):
+        lib = ctypes.CDLL(path)
+        lib.hd_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        lib.hd_probe_mfma_bf16.restype = ctypes.c_double
+        blocks, iters = 4096, 2048
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        lib.hd_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()), st)
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fl = sum(lib.hd_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()), st) for _ in range(5))
+        e.record()
+        torch.cuda.synchronize()
+        if fl > 0:
+            out["mfma_bf16_TFLOPs"] = round(fl / s.elapsed_time(e) / 1e9, 1)
+    src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    out["copy_GBps"] = round(5 * 2 * src.numel() * 2 / s.elapsed_time(e) / 1e6, 1)
+    return out
 
 
 def measured_traffic(name):
@@ -368,6 +403,7 @@ def main():
         "roofline": roof,
         "roofline_decode": roof_dec,
         "cpu_baseline": None if args.no_cpu else cpu_baseline(args.cpu_seconds),
+        "measured_peaks": None if only else measured_peaks(dev),
     }
     print(json.dumps(line), flush=True)
 

@@ -1,7 +1,9 @@
 """Build libhd.so (the HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
 ``python -m latent_sequence_length_amd.build`` compiles every ``csrc/*.hip``
-into ``_build/*.o`` in parallel and links ``latent_sequence_length_amd/libhd.so``.
+into ``_build/*.o`` in parallel and links ``latent_sequence_length_amd/libhd.so``;
+``probe/peak.hip`` (the measured matrix-core peak the benchmark reports beside
+the published one) becomes ``libhd_probe.so``.
 """
 import concurrent.futures as cf
 import os
@@ -13,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libhd.so")
+PROBE_SRC = os.path.join(PKG, "probe", "peak.hip")
+PROBE_LIB = os.path.join(PKG, "libhd_probe.so")
 ARCH = os.environ.get("HD_OFFLOAD_ARCH", "gfx950")
 
 # Packed-FP32 VALU ops are switched off for device code: hipcc would otherwise
@@ -58,6 +62,14 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp"
+    cmd = ["hipcc", *CFLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
