@@ -283,6 +283,15 @@ def main():
             hd.hd_rope(k, k, 10000.0)
 
         comps["rope_qk"] = (run_rope, 0.0, 2 * 2 * (q.numel() + k.numel()))
+    if want("rope_fwd_intra_n4"):
+        # the headline layer with RoPE fused: k rotated into k_rot, q rotated
+        # inside the prefill kernel (compare rope_qk + intra_n4)
+        q, k, v = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+        o, k_rot = torch.empty_like(q), torch.empty_like(k)
+        fl = useful_flops(I.B, I.L, I.n, I.Hq, I.d, I.mode, I.window)
+        by = 2 * (2 * q.numel() + 3 * k.numel() + v.numel())
+        comps["rope_fwd_intra_n4"] = (lambda q=q, k=k, v=v, o=o, kr=k_rot: hd.hd_sfa_fwd_rope(q, k, v, o, kr, I.n, I.mode),
+                                      fl, by)
     if want("decode_intra") or want("decode_cross"):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)

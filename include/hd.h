@@ -74,6 +74,23 @@ hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n,
                           void *out, void *stream);
 
 /*
+ * Prefill with the rotary embedding of the expanded positions fused in
+ * ("Multi-Stream Expansion and Training Objective": contiguous RoPE positions
+ * over the expanded sequence): k is rotated into k_rot (exactly hd_rope with
+ * pos_base = NULL), q is rotated inside the attention kernel right after it
+ * is loaded (no rotated q is written), then attention runs as hd_sfa_fwd on
+ * the rotated q and k_rot.  Same arguments as hd_sfa_fwd plus
+ *   k_rot  [B][n*L][Hkv][d] (dtype dt): output, the rotated keys (the rows a
+ *          decode cache holds); may equal k (k is then rotated in place)
+ *   theta  RoPE base (> 0), as in hd_rope
+ * The in-kernel rotation of q reduces the angle in double and uses the
+ * hardware sine / cosine; it agrees with hd_rope to the bf16 rounding of q.
+ */
+hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, float *lse, void *k_rot,
+                          int B, int L, int n, int Hq, int Hkv, int d, hd_mode mode, int window, float scale,
+                          float theta, hd_dtype dt, void *stream);
+
+/*
  * Rotary position embedding at the expanded positions ("Multi-Stream
  * Expansion and Training Objective": the expanded sequence is fed to the
  * Transformer with contiguous RoPE positions, so S_t is rotated by its

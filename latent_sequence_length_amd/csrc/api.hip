@@ -135,6 +135,11 @@ static void layer_map(A &a, int L, int n, hd_mode mode, int window, bool final_o
         a.weff = wcross;
     }
 }
+
+// Rotary frequencies in turns: ft[c] = theta^(-2c/d) / (2 pi), c < d/2.
+static void rope_freqs(double *ft, int d, float theta) {
+    for (int c = 0; c < d / 2; ++c) ft[c] = std::pow((double)theta, -2.0 * c / d) / (2.0 * 3.14159265358979323846);
+}
 }  // extern "C++"
 
 hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int L, int n,
@@ -180,6 +185,38 @@ hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o,
     return device_status(e, "sfa_fwd_final launch");
 }
 
+hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, float *lse, void *k_rot, int B,
+                          int L, int n, int Hq, int Hkv, int d, hd_mode mode, int window, float scale, float theta,
+                          hd_dtype dt, void *stream) {
+    if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
+    if (!(theta > 0.f) || !std::isfinite(theta)) return fail(HD_ERR_INVALID, "theta=%g must be > 0", (double)theta);
+    HD_TRY(check_ptr(q, "q"));
+    HD_TRY(check_ptr(k, "k"));
+    HD_TRY(check_ptr(v, "v"));
+    HD_TRY(check_ptr(o, "o"));
+    HD_TRY(check_ptr(k_rot, "k_rot"));
+    if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hd::RopeArgs ra{};  // k -> k_rot at positions 0 .. n*L-1
+    ra.x = k; ra.out = k_rot; ra.pos_base = nullptr; ra.pos_mul = 0;
+    ra.B = B; ra.T = n * L; ra.H = Hkv; ra.d = d;
+    rope_freqs(ra.freq_turns, d, theta);
+    hipError_t e = hd::launch_rope(ra, dt == HD_BF16, st);
+    if (e != hipSuccess) return device_status(e, "rope launch");
+    hd::FwdArgs a{};
+    a.q = q; a.k = k_rot; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+    layer_map(a, L, n, mode, window, false);
+    a.scale = resolve_scale(scale, d);
+    a.rope = 1;
+    rope_freqs(a.rope_ft, d, theta);
+    e = (dt == HD_BF16) ? hd::launch_sfa_fwd_bf16(a, st) : hd::launch_sfa_fwd_f32(a, st);
+    return device_status(e, "sfa_fwd_rope launch");
+}
+
 hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,
                   float theta, hd_dtype dt, void *stream) {
     if (B < 1 || T < 1 || H < 1) return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d T=%d H=%d)", B, T, H);
@@ -194,8 +231,7 @@ hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const in
     hd::RopeArgs a{};
     a.x = x; a.out = out; a.pos_base = pos_base; a.pos_mul = pos_mul;
     a.B = B; a.T = T; a.H = H; a.d = d;
-    for (int c = 0; c < d / 2; ++c)
-        a.freq_turns[c] = std::pow((double)theta, -2.0 * c / d) / (2.0 * 3.14159265358979323846);
+    rope_freqs(a.freq_turns, d, theta);
     return device_status(hd::launch_rope(a, dt == HD_BF16, static_cast<hipStream_t>(stream)), "rope launch");
 }
 

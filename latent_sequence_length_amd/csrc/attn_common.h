@@ -46,6 +46,30 @@ __device__ __forceinline__ int swz128(int r) { return ((r & 7) << 1) | ((r >> 3)
 // of the 256-byte bank window (and is a permutation over any 16 rows).
 __device__ __forceinline__ int swzv(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// Rotary embedding (rotate-half) of a query row held as MFMA operands: lane
+// half hi holds dims 16*ks + 8*hi + e (e < 8) in qop[ks]; dim c pairs with
+// c + D/2, i.e. k-step ks with ks + D/32 of the same lane.  The angle pos*f_c
+// is taken in turns (ft[c] = f_c / 2 pi), reduced to [-1/2, 1/2] in double
+// and fed to the hardware sine / cosine, whose input is in turns.  ft is read
+// at lane-uniform indices only (both halves' entries, then a select).
+template <int D>
+__device__ __forceinline__ void rope_rotate_q(bf16x8 (&qop)[D / 16], int64_t pos, const double *ft, int hi) {
+    constexpr int KH = D / 32;
+    const double dpos = (double)pos;
+#pragma unroll
+    for (int ks = 0; ks < KH; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double f = hi ? ft[16 * ks + 8 + e] : ft[16 * ks + e];
+            const double turns = dpos * f;
+            const float red = (float)(turns - rint(turns));
+            const float sn = __builtin_amdgcn_sinf(red), cs = __builtin_amdgcn_cosf(red);
+            const float x0 = (float)qop[ks][e], x1 = (float)qop[ks + KH][e];
+            qop[ks][e] = (bf16)(x0 * cs - x1 * sn);
+            qop[ks + KH][e] = (bf16)(x1 * cs + x0 * sn);
+        }
+}
+
 __device__ __forceinline__ float pair_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));

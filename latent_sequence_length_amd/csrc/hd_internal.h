@@ -58,6 +58,10 @@ struct FwdArgs {
     int qsub;     // Q rows between the first queries of consecutive sub-sequences
     int qstride;  // Q rows between consecutive queries
     int qmul, qadd;
+    // rotary embedding of q at its expanded position, applied after the load
+    // (0 = q is used as given); rope_ft[c] = theta^(-2c/d) / (2 pi), c < d/2
+    int rope;
+    double rope_ft[64];
 };
 hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st);

@@ -36,6 +36,18 @@ __global__ __launch_bounds__(64) void sfa_fwd_f32_kernel(FwdArgs p) {
     for (int c = 0; c < D; ++c) { qv[c] = qp[c]; acc[c] = 0.f; }
     float m = -INFINITY, l = 0.f;
     const int lim = i * p.qmul + p.qadd;  // last visible key element
+    if (p.rope) {  // rotate-half at the query's expanded position, angle reduced in double
+        const double pos = (double)(p.kbase + sub + (int64_t)lim * p.stride);
+#pragma unroll
+        for (int c = 0; c < D / 2; ++c) {
+            const double turns = pos * p.rope_ft[c];
+            float sn, cs;
+            sincosf((float)(turns - rint(turns)) * 6.28318530717958647692f, &sn, &cs);
+            const float x0 = qv[c], x1 = qv[c + D / 2];
+            qv[c] = x0 * cs - x1 * sn;
+            qv[c + D / 2] = x1 * cs + x0 * sn;
+        }
+    }
     const int jbeg = p.weff ? max(0, lim - p.weff + 1) : 0;
     for (int j = jbeg; j <= lim; ++j) {
         const int64_t off = ((kpos0 + (int64_t)j * p.stride) * p.Hkv + kvh) * D;

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
             qop[ks] = qvalid ? x : bf16x8{};
         }
+        if (p.rope) rope_rotate_q<D>(qop, p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
     }
 
     f32x16 oacc[D / 32];
@@ -373,7 +374,8 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
 
 // GQ: the query map is not the identity (qmul, qadd) != (1, 0); a full layer
 // runs the GQ = false instance, whose band tests are the plain p <= j ones.
-template <bool GQ>
+// ROPE: q is rotated at its expanded position right after the load.
+template <bool GQ, bool ROPE>
 __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
                                                                   float scale_log2) {
     constexpr int D = 128;
@@ -486,6 +488,8 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
             qop[ks] = qvalid ? x : bf16x8{};
         }
+        // expanded position of the query: key element lim(p) of this sub-sequence
+        if (ROPE) rope_rotate_q<D>(qop, p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
     }
 
     D128State st;
@@ -551,12 +555,10 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
                 const int nqblk2 = (a.Lq + QW * TB2 - 1) / (QW * TB2);
                 const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
                 if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
-                if (a.qmul != 1 || a.qadd != 0)
-                    hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel<true>, dim3((unsigned)grid2), dim3(64 * D128_NW), 0,
-                                       st, a, HG, TB2, nqblk2, sl2);
-                else
-                    hipLaunchKernelGGL(sfa_fwd_bf16_d128_kernel<false>, dim3((unsigned)grid2), dim3(64 * D128_NW), 0,
-                                       st, a, HG, TB2, nqblk2, sl2);
+                const bool gq = a.qmul != 1 || a.qadd != 0;
+                auto kern = gq ? (a.rope ? sfa_fwd_bf16_d128_kernel<true, true> : sfa_fwd_bf16_d128_kernel<true, false>)
+                               : (a.rope ? sfa_fwd_bf16_d128_kernel<false, true> : sfa_fwd_bf16_d128_kernel<false, false>);
+                hipLaunchKernelGGL(kern, dim3((unsigned)grid2), dim3(64 * D128_NW), 0, st, a, HG, TB2, nqblk2, sl2);
             }
             break;
         default:

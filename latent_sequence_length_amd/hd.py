@@ -40,6 +40,7 @@ def load():
     lib.hd_expand_embed.argtypes = [P, I, I, I, P, I64, I, I, P, P]
     lib.hd_sfa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
     lib.hd_sfa_fwd_final.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P]
+    lib.hd_sfa_fwd_rope.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, I, P]
     lib.hd_sfa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.hd_sfa_decode_workspace_bytes.restype = SZ
     lib.hd_sfa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
@@ -50,8 +51,8 @@ def load():
     lib.hd_sfa_bwd_final_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd_final.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
-    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_decode, lib.hd_sfa_bwd,
-              lib.hd_sfa_bwd_final, lib.hd_rope):
+    for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_fwd_rope, lib.hd_sfa_decode,
+              lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -160,6 +161,30 @@ def hd_sfa_fwd_final(q, k, v, o, n, mode, window=0, scale=0.0, lse=None):
     _check(load().hd_sfa_fwd_final(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lp,
                                    B, L, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt, _stream(q)))
     return o
+
+
+def hd_sfa_fwd_rope(q, k, v, o, k_rot, n, mode, window=0, scale=0.0, theta=10000.0, lse=None):
+    """Prefill with RoPE at the expanded positions fused in: k rotated into
+    k_rot, q rotated inside the kernel; o (and lse) as hd_sfa_fwd."""
+    B, nL, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if nL % n:
+        raise ValueError(f"sequence length {nL} is not a multiple of n={n}")
+    if k.shape != (B, nL, Hkv, d) or v.shape != k.shape or o.shape != q.shape or k_rot.shape != k.shape:
+        raise ValueError("shape mismatch among q, k, v, o, k_rot")
+    dt = _dtype_code(q)
+    for t, name in ((k, "k"), (v, "v"), (o, "o"), (k_rot, "k_rot")):
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q's {q.dtype}")
+    lp = None
+    if lse is not None:
+        if lse.shape != (B, Hq, nL):
+            raise ValueError(f"lse must be {(B, Hq, nL)}")
+        lp = _dev(lse, "lse", torch.float32)
+    _check(load().hd_sfa_fwd_rope(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), lp, _dev(k_rot, "k_rot"),
+                                  B, nL // n, n, Hq, Hkv, d, int(mode), int(window), float(scale), float(theta), dt,
+                                  _stream(q)))
+    return o, k_rot
 
 
 def hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap):
@@ -287,6 +312,16 @@ def sfa_fwd(q, k, v, n, mode, window=0, scale=0.0, return_lse=False):
         lse = torch.empty((B, Hq, nL), dtype=torch.float32, device=q.device)
     hd_sfa_fwd(q, k, v, o, n, mode, window, scale, lse)
     return (o, lse) if return_lse else o
+
+
+def sfa_fwd_rope(q, k, v, n, mode, window=0, scale=0.0, theta=10000.0, return_lse=False):
+    o, k_rot = torch.empty_like(q), torch.empty_like(k)
+    lse = None
+    if return_lse:
+        B, nL, Hq, _ = q.shape
+        lse = torch.empty((B, Hq, nL), dtype=torch.float32, device=q.device)
+    hd_sfa_fwd_rope(q, k, v, o, k_rot, n, mode, window, scale, theta, lse)
+    return (o, k_rot, lse) if return_lse else (o, k_rot)
 
 
 def sfa_fwd_final(q, k, v, n, mode, window=0, scale=0.0, return_lse=False):

@@ -32,7 +32,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_fwd_rope", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_bwd_final_workspace_bytes", "hd_sfa_bwd_final",
         "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
         "hd_status_string", "hd_last_error", "hd_version"])
@@ -75,6 +75,24 @@ def fwd(lib, entry="hd_sfa_fwd", **kw):
 @pytest.mark.parametrize("entry", ["hd_sfa_fwd", "hd_sfa_fwd_final"])
 def test_fwd_validation(lib, kw, code, entry):
     assert fwd(lib, entry, **kw) == code
+    assert hd.last_error() != ""
+
+
+def fwd_rope(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, k_rot=FAKE, B=1, L=8, n=2, Hq=4, Hkv=2, d=64,
+             mode=0, window=0, scale=0.0, theta=10000.0, dt=0, stream=None)
+    a.update(kw)
+    return lib.hd_sfa_fwd_rope(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(theta=0.0), hd.HD_ERR_INVALID), (dict(theta=-1.0), hd.HD_ERR_INVALID),
+    (dict(theta=float("inf")), hd.HD_ERR_INVALID), (dict(k_rot=None), hd.HD_ERR_INVALID),
+    (dict(k_rot=FAKE + 8), hd.HD_ERR_INVALID), (dict(B=0), hd.HD_ERR_INVALID), (dict(Hq=3), hd.HD_ERR_INVALID),
+    (dict(d=96), hd.HD_ERR_UNSUPPORTED), (dict(mode=2), hd.HD_ERR_UNSUPPORTED),
+])
+def test_fwd_rope_validation(lib, kw, code):
+    assert fwd_rope(lib, **kw) == code
     assert hd.last_error() != ""
 
 

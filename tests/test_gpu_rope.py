@@ -80,3 +80,69 @@ def test_rope_then_attention(dtype, mode):
         assert err.max() <= 1e-4
     else:
         assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+INTRA, CROSS = 0, 1
+
+
+def rope_oracle_fwd(q, k, v, n, mode, window, dtype, rows=None):
+    """The oracle's rotation (double, rounded to the input dtype RNE) composed
+    with its attention (all rows, or the flat query rows given)."""
+    qo = torch.from_numpy(oracle.rope(q.cpu(), 10000.0)).to(dtype)
+    ko = torch.from_numpy(oracle.rope(k.cpu(), 10000.0)).to(dtype)
+    if rows is None:
+        return oracle.sfa_fwd(qo, ko, v.cpu(), n, mode, window)
+    return oracle.sfa_rows(qo, ko, v.cpu(), n, mode, window, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("shape,mode,window", [
+    ((1, 96, 4, 8, 2, 128), INTRA, 0), ((1, 96, 4, 8, 2, 128), CROSS, 0),
+    ((2, 70, 3, 4, 4, 64), CROSS, 5), ((1, 130, 2, 4, 2, 32), INTRA, 7), ((1, 200, 1, 4, 1, 128), CROSS, 0),
+])
+def test_fwd_rope_vs_oracle(shape, mode, window, dtype):
+    """hd_sfa_fwd_rope: k_rot is hd_rope's output bit for bit; o and lse match
+    the oracle's rotation + attention within the prefill's bars."""
+    B, L, n, Hq, Hkv, d = shape
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, dtype, DEV)
+    o, k_rot, lse = hd.sfa_fwd_rope(q, k, v, n, mode, window, return_lse=True)
+    assert torch.equal(k_rot, hd.rope(k, 10000.0))
+    want, wlse = rope_oracle_fwd(q, k, v, n, mode, window, dtype)
+    err = np.abs(o.double().cpu().numpy() - want)
+    lerr = np.abs(lse.double().cpu().numpy() - wlse)
+    sys.__stdout__.write(f"  o max {err.max():.3e} mean {err.mean():.3e}; lse max {lerr.max():.3e}\n")
+    if dtype == torch.float32:
+        assert err.max() <= 1e-4 and lerr.max() <= 1e-4
+    else:
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2.5e-3
+
+
+def test_fwd_rope_in_place_and_final_layout():
+    """k_rot may be k itself (rotated in place): same o, and k then holds k_rot."""
+    B, L, n, Hq, Hkv, d = 1, 150, 4, 8, 2, 128
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.bfloat16, DEV)
+    o, k_rot = hd.sfa_fwd_rope(q, k, v, n, CROSS, 0)
+    kc = k.clone()
+    o2 = torch.empty_like(q)
+    hd.hd_sfa_fwd_rope(q, kc, v, o2, kc, n, CROSS)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(kc, k_rot)
+
+
+def test_fwd_rope_full_size_sampled():
+    """The 4096-token intra-stream layer (n=4, 32 q / 8 kv heads, d=128) with
+    RoPE fused: 4096 sampled rows (expanded positions up to 16383) against the
+    oracle's rotation + attention."""
+    c = synth.INTRA_4K
+    q, k, v = synth.qkv(c.B, c.L, c.n, c.Hq, c.Hkv, c.d, c.dtype, DEV)
+    o, _ = hd.sfa_fwd_rope(q, k, v, c.n, c.mode, c.window)
+    nL = c.n * c.L
+    rng = np.random.default_rng(12)
+    edge_t = [0, 1, 2, 3, 4, 5, nL - 1, nL - 2, nL - 5, 8191, 8192, 256, 257]
+    rows = np.unique(np.concatenate([np.array([t * c.Hq + h for t in edge_t for h in (0, c.Hq - 1)]),
+                                     rng.integers(0, nL * c.Hq, 4096)]))
+    want, _ = rope_oracle_fwd(q, k, v, c.n, c.mode, c.window, c.dtype, rows=rows)
+    got = o.reshape(-1, c.d)[torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
+    err = np.abs(got - want)
+    sys.__stdout__.write(f"  rows max {err.max():.3e} mean {err.mean():.3e}\n")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
