@@ -233,6 +233,19 @@ def sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, sca
     return o
 
 
+def sfa_decode_final(q_final, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, scale=0.0):
+    """Decode step of a KV-mirror layer: only the final stream's query
+    q_final [B, 1, Hq, d] (at expanded position len*n + n-1) is run; the
+    answer is that row of ``sfa_decode`` (a query row's attention does not
+    depend on the other streams' queries).  Returns o [B, 1, Hq, d]."""
+    qb, _ = _buf(q_final)
+    n = tuple(k_new.shape)[1]
+    q = np.zeros((qb.shape[0], n) + qb.shape[2:], dtype=qb.dtype)
+    q[:, n - 1] = qb[:, 0]
+    o = sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window, scale)
+    return np.ascontiguousarray(o[:, n - 1:n])
+
+
 def decode_append(x_new, cache, cache_len):
     """Return a copy of cache with x_new written at token cache_len[b] (bytewise)."""
     xb, _ = _buf(x_new)

@@ -709,3 +709,23 @@ def test_final_bwd_invariants(oracle, mode, W):
         keep = np.zeros(n * L, dtype=bool)
         keep[n - 1::n] = True
         assert np.abs(dk[:, ~keep]).max() == 0.0 and np.abs(dv[:, ~keep]).max() == 0.0
+
+
+@pytest.mark.parametrize("mode,W", [(INTRA, 0), (CROSS, 0), (INTRA, 2), (CROSS, 1)])
+def test_decode_final_equals_final_prefill_rows(oracle, mode, W):
+    """A KV-mirror layer's decode step (final-stream query only) equals the
+    final-stream prefill's last row on the appended sequence."""
+    B, n, Hq, Hkv, d, T_cap = 3, 3, 4, 2, 8, 9
+    q, kn, vn, kc, vc = synth.decode_inputs(B, n, Hq, Hkv, d, T_cap, torch.float32)
+    qf = q[:, n - 1:n].contiguous()
+    lens = [0, 4, 8]
+    o = oracle.sfa_decode_final(qf, kn, vn, kc, vc, lens, mode, W)
+    assert o.shape == (B, 1, Hq, d)
+    for b, ln in enumerate(lens):
+        L = ln + 1
+        kseq = torch.cat([kc[b, :ln], kn[b:b + 1]], 0).reshape(1, L * n, Hkv, d)
+        vseq = torch.cat([vc[b, :ln], vn[b:b + 1]], 0).reshape(1, L * n, Hkv, d)
+        qseq = torch.zeros(1, L, Hq, d)
+        qseq[0, ln] = qf[b, 0]
+        of, _ = oracle.sfa_final(qseq, kseq, vseq, n, mode, W)
+        np.testing.assert_allclose(o[b, 0], of[0, ln], rtol=0, atol=1e-14)
