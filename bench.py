@@ -292,7 +292,7 @@ def main():
         by = 2 * (2 * q.numel() + 3 * k.numel() + v.numel())
         comps["rope_fwd_intra_n4"] = (lambda q=q, k=k, v=v, o=o, kr=k_rot: hd.hd_sfa_fwd_rope(q, k, v, o, kr, I.n, I.mode),
                                       fl, by)
-    if want("decode_intra") or want("decode_cross"):
+    if want("decode_intra") or want("decode_cross") or want("decode_final_intra") or want("decode_final_cross"):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)
         dcl = torch.full((Dc.B,), Dc.ctx, dtype=torch.int32, device=dev)
@@ -315,6 +315,17 @@ def main():
                 comps[name] = (lambda mode=mode: hd.hd_sfa_decode(dq, dkn, dvn, dkc, dvc, dcl, do, mode, 0, 0.0, ws),
                                fl, by)
                 del g
+        # KV-mirror layers: the final stream's query only (intra reads stream
+        # n-1's cache rows alone, cross the whole cache)
+        dqf = dq[:, Dc.n - 1:Dc.n].contiguous()
+        dof = torch.empty_like(dqf)
+        for mode, name in ((0, "decode_final_intra"), (1, "decode_final_cross")):
+            if want(name):
+                rows = Dc.ctx if mode == 0 else Dc.ctx * Dc.n
+                by_f = 2 * rows * Dc.Hkv * Dc.d * 2 * Dc.B + 2 * 2 * dqf.numel() + 2 * dkn.numel() * 2 * 2
+                pairs = Dc.B * Dc.Hq * ((Dc.ctx + 1) if mode == 0 else (Dc.ctx + 1) * Dc.n)
+                comps[name] = (lambda mode=mode: hd.hd_sfa_decode(dqf, dkn, dvn, dkc, dvc, dcl, dof, mode, 0, 0.0, ws,
+                                                                  final_only=True), 4.0 * Dc.d * pairs, by_f)
     if want("embed"):
         tabs = synth.tables(E["n"], E["V"], E["D"], E["dtype"], dev)
         # 64 rotating id sets so rows come from HBM rather than the last-level cache

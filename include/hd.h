@@ -234,6 +234,25 @@ hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new,
                         hd_mode mode, int window, float scale, hd_dtype dt,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * One decode step of a KV-mirror layer ("Persistent KV and the KV-mirror
+ * Saving": only the supervised final stream is run through a mirrored layer;
+ * its K/V, of every stream, come from the paired early layer).  As
+ * hd_sfa_decode, with only the final stream's query:
+ *   q, o   [B][1][Hq][d]: the query / output of stream n-1 of the new token,
+ *          at expanded position len*n + n-1
+ *   k_new, v_new  [B][n][Hkv][d]: all n streams' rows, appended as in
+ *          hd_sfa_decode (the cache layout is shared)
+ * Intra layers read only stream n-1's cache rows (1/n of the cache bytes);
+ * cross layers read every row.  The workspace is the one hd_sfa_decode
+ * needs for the same sizes (hd_sfa_decode_workspace_bytes).  Same
+ * requirements and errors, with Hq/Hkv <= 64.
+ */
+hd_status hd_sfa_decode_final(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                              const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                              hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Static name of a status code. */
 const char *hd_status_string(hd_status s);
 

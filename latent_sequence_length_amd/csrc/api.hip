@@ -299,14 +299,14 @@ size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T
     return hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);
 }
 
-hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
-                        const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
-                        hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+static hd_status sfa_decode_common(const void *q, const void *k_new, const void *v_new, void *k_cache,
+                                   void *v_cache, const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq,
+                                   int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt,
+                                   void *workspace, size_t workspace_bytes, void *stream, bool final_only) {
     HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
     if (T_cap < 1) return fail(HD_ERR_INVALID, "T_cap=%d < 1", T_cap);
-    if (n * (Hq / Hkv) > 64)
-        return fail(HD_ERR_UNSUPPORTED, "n*(Hq/Hkv)=%d query rows per kv head above 64", n * (Hq / Hkv));
+    const int qrows = (final_only ? 1 : n) * (Hq / Hkv);
+    if (qrows > 64) return fail(HD_ERR_UNSUPPORTED, "%d query rows per kv head above 64", qrows);
     HD_TRY(check_ptr(q, "q"));
     HD_TRY(check_ptr(k_new, "k_new"));
     HD_TRY(check_ptr(v_new, "v_new"));
@@ -320,16 +320,39 @@ hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new, voi
     a.B = B; a.n = n; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.T_cap = T_cap;
     a.mode = (int)mode; a.window = window;
     a.scale = resolve_scale(scale, d);
+    if (final_only) {
+        // the final stream's query only; an intra layer shows it stream n-1's keys alone
+        a.qs0 = n - 1; a.nqs = 1; a.rpt = (mode == HD_MODE_INTRA) ? 1 : n;
+    } else {
+        a.qs0 = 0; a.nqs = n; a.rpt = n;
+    }
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const char *what = final_only ? "sfa_decode_final launch" : "sfa_decode launch";
     if (dt == HD_BF16) {
         const size_t need = hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);
         if (workspace_bytes < need)
             return fail(HD_ERR_INVALID, "workspace of %zu bytes below the %zu required", workspace_bytes, need);
         HD_TRY(check_ptr(workspace, "workspace"));
         a.ws = static_cast<float *>(workspace);
-        return device_status(hd::launch_sfa_decode_bf16(a, st), "sfa_decode launch");
+        return device_status(hd::launch_sfa_decode_bf16(a, st), what);
     }
-    return device_status(hd::launch_sfa_decode_f32(a, st), "sfa_decode launch");
+    return device_status(hd::launch_sfa_decode_f32(a, st), what);
+}
+
+hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                        const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                        hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return sfa_decode_common(q, k_new, v_new, k_cache, v_cache, cache_len, T_cap, o, B, n, Hq, Hkv, d, mode, window,
+                             scale, dt, workspace, workspace_bytes, stream, false);
+}
+
+hd_status hd_sfa_decode_final(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                              const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                              hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    return sfa_decode_common(q, k_new, v_new, k_cache, v_cache, cache_len, T_cap, o, B, n, Hq, Hkv, d, mode, window,
+                             scale, dt, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -108,6 +108,12 @@ struct DecArgs {
     int mode;           // 0 intra, 1 cross
     int window;         // tokens, 0 = none
     float scale;
+    // queries: streams qs0 .. qs0+nqs-1 of the new token (all n, or only the
+    // final stream of a KV-mirror layer); q, o are [B][nqs][Hq][d]
+    int qs0, nqs;
+    // cache rows scanned per token: n, or 1 when only stream qs0's keys can be
+    // visible (an intra layer's final-stream query)
+    int rpt;
 };
 size_t decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T_cap);
 hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st);

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
     const int split = blockIdx.x;
     const int bh = blockIdx.y;
     const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
-    const int n = p.n, g = p.Hq / p.Hkv, QR = n * g;
+    const int n = p.n, g = p.Hq / p.Hkv, QR = p.nqs * g;
     const int len = p.cache_len[b];
     const int c0 = split * sp.chunk;
     if (c0 > len) return;  // nothing cached here yet; the combine skips it
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
     const int iters = (nblk + NW - 1) / NW;
 
     // Query operands: block qb, lane column l16 is query row c = qb*16 + l16
-    // (row c <-> stream c / g, head kvh*g + c % g); slots grp hold dims
+    // (row c <-> stream qs0 + c / g, head kvh*g + c % g); slots grp hold dims
     // ks*32 + 8*grp .. +7.
     const bf16 *qg = static_cast<const bf16 *>(p.q);
     bf16x8 qop[NQB][D / 32];
@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
     for (int qb = 0; qb < NQB; ++qb) {
         const int c = qb * 16 + l16;
         const bool ok = c < QR;
-        const int s = ok ? c / g : 0, hh = ok ? c - s * g : 0;
-        qstream[qb] = s;
-        const bf16 *qp = qg + (((int64_t)b * n + s) * p.Hq + kvh * g + hh) * D + 8 * grp;
+        const int sr = ok ? c / g : 0, hh = ok ? c - sr * g : 0;  // query stream qs0 + sr
+        qstream[qb] = p.qs0 + sr;
+        const bf16 *qp = qg + (((int64_t)b * p.nqs + sr) * p.Hq + kvh * g + hh) * D + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 32);
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
     const int l16 = lane & 15, grp = lane >> 4;
     const int split = blockIdx.x, bh = blockIdx.y;
     const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
-    const int n = p.n, g = p.Hq / p.Hkv, QR = n * g;
+    const int n = p.n, g = p.Hq / p.Hkv, QR = p.nqs * g;
     const int len = p.cache_len[b];
     const int c0 = split * sp.chunk;
     if (c0 > len) return;  // nothing cached here yet; the combine skips it
@@ -357,34 +357,37 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
         }
     }
 
-    // Rows (flat token*n + stream) of this chunk inside the window.
+    // Rows of this chunk inside the window: flat token*n + stream, or (rpt = 1)
+    // one row per token, of stream qs0 only.
+    const int rpt = p.rpt;
+    const int sbase = (rpt == 1) ? p.qs0 : 0;  // stream of a token's first scanned row
     const int tlo = p.window ? max(c0, len - p.window) : c0;
-    const int row_lo = tlo * n, row_hi = c1 * n;
+    const int row_lo = tlo * rpt, row_hi = c1 * rpt;
     const int ntiles = row_hi > row_lo ? (row_hi - row_lo + DT_ROWS - 1) / DT_ROWS : 0;
 
     // Copy-in mapping: wave w, instruction i covers slots (4w+i)*64 .. +63 of
-    // the tile (slot = row*16 + physical chunk); n divides 64, so the row's
+    // the tile (slot = row*16 + physical chunk); rpt divides 64, so the row's
     // token offset and stream are fixed per lane.
     int ltok[4], lstream[4], lchunk[4], lrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = (wave * 4 + i) * 4 + (lane >> 4);
         lrow[i] = r;
-        ltok[i] = r / n;
-        lstream[i] = r - ltok[i] * n;
+        ltok[i] = r / rpt;
+        lstream[i] = sbase + r - ltok[i] * rpt;
         lchunk[i] = ((lane & 15) ^ swz128(r)) * 8;
     }
-    const int tok_per_tile = DT_ROWS / n;
+    const int tok_per_tile = DT_ROWS / rpt;
     auto issue = [&](int t) {
         char *dst = smem + (t % DT_NBUF) * 2 * DT_TILE;
         const int tok0 = tlo + t * tok_per_tile;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             int tok = tok0 + ltok[i];
-            const int last = (row_hi - 1) / n;  // rows past the chunk re-read its last token
-            const bool past = (tok - tlo) * n + lstream[i] >= row_hi - row_lo;
+            const int last = (row_hi - 1) / rpt;  // rows past the chunk re-read its last row
+            const bool past = (tok - tlo) * rpt + (lstream[i] - sbase) >= row_hi - row_lo;
             tok = past ? last : tok;
-            const int s = past ? (row_hi - 1) - last * n : lstream[i];
+            const int s = past ? sbase + (row_hi - 1) - last * rpt : lstream[i];
             const int64_t coff = cache_b + (int64_t)tok * cache_tok + (int64_t)s * hstride + lchunk[i];
             const int64_t noff = new_b + (int64_t)s * hstride + lchunk[i];
             const bool is_new = tok >= len;
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
         }
     };
     // Query operands: block qb, lane column l16 is query row c = qb*16 + l16
-    // (row c <-> stream c / g, head kvh*g + c % g); slots grp hold dims
+    // (row c <-> stream qs0 + c / g, head kvh*g + c % g); slots grp hold dims
     // ks*32 + 8*grp .. +7.
     const bf16 *qg = static_cast<const bf16 *>(p.q);
     bf16x8 qop[NQB][D / 32];
@@ -405,9 +408,9 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
     for (int qb = 0; qb < NQB; ++qb) {
         const int c = qb * 16 + l16;
         const bool ok = c < QR;
-        const int s = ok ? c / g : 0, hh = ok ? c - s * g : 0;
-        qstream[qb] = s;
-        const bf16 *qp = qg + (((int64_t)b * n + s) * p.Hq + kvh * g + hh) * D + 8 * grp;
+        const int sr = ok ? c / g : 0, hh = ok ? c - sr * g : 0;  // query stream qs0 + sr
+        qstream[qb] = p.qs0 + sr;
+        const bf16 *qp = qg + (((int64_t)b * p.nqs + sr) * p.Hq + kvh * g + hh) * D + 8 * grp;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
             const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 32);
@@ -475,8 +478,8 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = rtile + i;
-                const int tok = r / n;
-                const int sk = r - tok * n;
+                const int tok = r / rpt;
+                const int sk = sbase + r - tok * rpt;
                 bool vis = r < row_hi;
                 if (p.mode == 0) vis = vis && sk == sq && (p.window == 0 || len - tok < p.window);
                 else vis = vis && r <= tq && (p.window == 0 || tq - r < (int64_t)n * p.window);
@@ -554,7 +557,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp) {
     const int lane = threadIdx.x & 63;
-    const int g = p.Hq / p.Hkv, QR = p.n * g;
+    const int g = p.Hq / p.Hkv, QR = p.nqs * g;
     const int64_t row = (int64_t)blockIdx.x * NW + (threadIdx.x >> 6);  // (bh, c)
     if (row >= (int64_t)p.B * p.Hkv * QR) return;
     const int c = (int)(row % QR);
@@ -581,8 +584,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp
             if (dim < D) acc[e] += wt * ws_acc[pk * D + dim];
         }
     }
-    const int s = c / g, hh = c - s * g;
-    bf16 *op = static_cast<bf16 *>(p.o) + (((int64_t)b * p.n + s) * p.Hq + kvh * g + hh) * D;
+    const int sr = c / g, hh = c - sr * g;  // query stream qs0 + sr
+    bf16 *op = static_cast<bf16 *>(p.o) + (((int64_t)b * p.nqs + sr) * p.Hq + kvh * g + hh) * D;
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -613,7 +616,7 @@ hipError_t launch_partial(const DecArgs &a, Split sp, float sl2, hipStream_t st)
 
 template <int D>
 hipError_t launch_d(const DecArgs &a, Split sp, float sl2, hipStream_t st) {
-    const int QR = a.n * (a.Hq / a.Hkv);
+    const int QR = a.nqs * (a.Hq / a.Hkv);
     hipError_t e;
     switch ((QR + 15) / 16) {
         case 1: e = launch_partial<D, 1>(a, sp, sl2, st); break;
@@ -646,7 +649,7 @@ hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st) {
     const float sl2 = a.scale * kLog2e;
     if (use_d128_path(a.n, a.d)) {
         const Split sp = choose_split_d128(a.B, a.Hkv, a.T_cap);
-        const int QR = a.n * (a.Hq / a.Hkv);
+        const int QR = a.nqs * (a.Hq / a.Hkv);
         hipError_t e;
         switch ((QR + 15) / 16) {
             case 1: e = launch_partial_d128<1>(a, sp, sl2, st); break;

@@ -73,12 +73,12 @@ __global__ __launch_bounds__(64) void sfa_fwd_f32_kernel(FwdArgs p) {
 // Decode: one thread per (b, s, h) query; also appends the new rows.
 template <int D>
 __global__ __launch_bounds__(64) void sfa_decode_f32_kernel(DecArgs p) {
-    const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, s, h)
-    const int64_t nrows = (int64_t)p.B * p.n * p.Hq;
+    const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;  // (b, query stream, h)
+    const int64_t nrows = (int64_t)p.B * p.nqs * p.Hq;
     if (row >= nrows) return;
     const int h = (int)(row % p.Hq);
-    const int s = (int)((row / p.Hq) % p.n);
-    const int b = (int)(row / p.Hq / p.n);
+    const int s = p.qs0 + (int)((row / p.Hq) % p.nqs);
+    const int b = (int)(row / p.Hq / p.nqs);
     const int g = p.Hq / p.Hkv, kvh = h / g;
     const int len = p.cache_len[b];
     const float *qg = static_cast<const float *>(p.q);
@@ -158,7 +158,7 @@ hipError_t launch_sfa_fwd_f32(const FwdArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_sfa_decode_f32(const DecArgs &a, hipStream_t st) {
-    const int64_t nrows = (int64_t)a.B * a.n * a.Hq;
+    const int64_t nrows = (int64_t)a.B * a.nqs * a.Hq;
     const unsigned grid = (unsigned)((nrows + 63) / 64);
     switch (a.d) {
         case 32: hipLaunchKernelGGL(sfa_decode_f32_kernel<32>, dim3(grid), dim3(64), 0, st, a); break;

@@ -44,6 +44,7 @@ def load():
     lib.hd_sfa_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.hd_sfa_decode_workspace_bytes.restype = SZ
     lib.hd_sfa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
+    lib.hd_sfa_decode_final.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_sfa_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.hd_sfa_bwd_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
@@ -52,7 +53,7 @@ def load():
     lib.hd_sfa_bwd_final.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
     for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_fwd_rope, lib.hd_sfa_decode,
-              lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
+              lib.hd_sfa_decode_final, lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -192,9 +193,14 @@ def hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap):
 
 
 def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=0, scale=0.0,
-                  workspace=None):
-    """One decode step: append k_new/v_new at cache_len, attend, write o."""
-    B, n, Hq, d = q.shape
+                  workspace=None, final_only=False):
+    """One decode step: append k_new/v_new at cache_len, attend, write o.
+    final_only: q and o are [B, 1, Hq, d], the final stream's query of a
+    KV-mirror layer (hd_sfa_decode_final)."""
+    B, nq, Hq, d = q.shape
+    n = k_new.shape[1]
+    if nq != (1 if final_only else n):
+        raise ValueError(f"q must be [B, {1 if final_only else n}, Hq, d]")
     Hkv = k_new.shape[2]
     T_cap = k_cache.shape[1]
     if k_new.shape != (B, n, Hkv, d) or v_new.shape != k_new.shape:
@@ -212,11 +218,12 @@ def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     wp = _dev(workspace, "workspace") if workspace is not None else None
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load().hd_sfa_decode(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
-                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                                _dev(cache_len, "cache_len", torch.int32), T_cap, _dev(o, "o"),
-                                B, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt,
-                                wp, wbytes, _stream(q)))
+    entry = load().hd_sfa_decode_final if final_only else load().hd_sfa_decode
+    _check(entry(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                 _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                 _dev(cache_len, "cache_len", torch.int32), T_cap, _dev(o, "o"),
+                 B, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt,
+                 wp, wbytes, _stream(q)))
     return o
 
 
@@ -337,6 +344,12 @@ def sfa_fwd_final(q, k, v, n, mode, window=0, scale=0.0, return_lse=False):
 def sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, scale=0.0, workspace=None):
     o = torch.empty_like(q)
     return hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window, scale, workspace)
+
+
+def sfa_decode_final(q, k_new, v_new, k_cache, v_cache, cache_len, mode, window=0, scale=0.0, workspace=None):
+    o = torch.empty_like(q)
+    return hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window, scale, workspace,
+                         final_only=True)
 
 
 def sfa_bwd(q, k, v, o, dout, lse, n, mode, window=0, scale=0.0):

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
         "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_fwd_rope", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_bwd_final_workspace_bytes", "hd_sfa_bwd_final",
-        "hd_sfa_decode_workspace_bytes", "hd_sfa_decode",
+        "hd_sfa_decode_workspace_bytes", "hd_sfa_decode", "hd_sfa_decode_final",
         "hd_status_string", "hd_last_error", "hd_version"])
 
 
@@ -113,6 +113,19 @@ def dec(lib, **kw):
 ])
 def test_decode_validation(lib, kw, code):
     assert dec(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T_cap=0), hd.HD_ERR_INVALID), (dict(cache_len=None), hd.HD_ERR_INVALID),
+    (dict(workspace_bytes=16), hd.HD_ERR_INVALID), (dict(d=48), hd.HD_ERR_UNSUPPORTED),
+    (dict(Hq=130, Hkv=2), hd.HD_ERR_UNSUPPORTED),   # 65 final-stream rows per kv head
+])
+def test_decode_final_validation(lib, kw, code):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, cache_len=FAKE, T_cap=16,
+             o=FAKE, B=2, n=4, Hq=8, Hkv=2, d=128, mode=1, window=0, scale=0.0, dt=0,
+             workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    assert lib.hd_sfa_decode_final(*a.values()) == code
 
 
 def test_workspace_size_is_monotone_and_zero_on_bad_sizes(lib):
