@@ -242,10 +242,14 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //   * the V^T operand comes from two ds_read_b64_tr_b16 per MFMA: within each
 //     16-lane group that instruction returns out[i][e] = in[4e + i/4][i%4],
 //     so lane j of the group addresses key row r0 + j/4, dims d0 + 4*(j%4);
-//   * softmax: the scale is folded into one fma before exp2, the running max
-//     is only raised when a tile's max exceeds it by more than 8 (log2 units),
-//     so the O rescale is skipped on almost every tile (p <= 2^8 keeps fp32
-//     sums and bf16 P exact enough; the final normalisation is unchanged);
+//   * softmax: the scale is folded into one fma before exp2; a tile's
+//     probabilities are taken against the running max as it stands and kept
+//     when every lane's share of its row sum stays <= 2^32 (no probability
+//     exceeds 2^32: harmless for fp32 sums and for bf16 P, whose relative
+//     precision does not depend on magnitude); otherwise, and on the first
+//     tile, the wave takes the tile max, rescales O and l and recomputes.
+//     The common tile needs no max, no rescale test and no O rescale; the
+//     final normalisation is unchanged;
 //   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
 //     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
 constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
@@ -304,7 +308,6 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
     __builtin_amdgcn_sched_barrier(0);
 
     __builtin_amdgcn_s_setprio(0);
-    float mx = -INFINITY;
     if (need_mask) {
         // visible <=> lo <= key <= hi, checked as one unsigned compare
         const int lo = p.weff ? mylim - p.weff + 1 : 0;
@@ -319,41 +322,56 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
                 sacc[kb][r] = (u <= span) ? sacc[kb][r] : -INFINITY;
             }
     }
-    {
+    // Probabilities against the running max; the tile is accepted as is when
+    // every lane's share of its row sum stays <= 2^32 (so no probability
+    // exceeds it), else -- and while some row has no max yet -- the wave
+    // raises every row's max to the tile's, rescales and recomputes.
+    bf16x8 pop[4];
+    float lsum = 0.f;
+    auto probs = [&](float neg_m) {
+        lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                bf16x8 pp;
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    pp[j] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 0, 1), kOnes2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 2, 3), kOnes2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 4, 5), kOnes2, lsum, false);
+                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 6, 7), kOnes2, lsum, false);
+                pop[kb * 2 + m2] = pp;
+            }
+    };
+    bool slow = true;
+    if (!__ballot(st.m_run == -INFINITY)) {
+        probs(-st.m_run);
+        slow = __ballot(!(lsum <= 4294967296.f)) != 0;  // also catches inf / NaN
+    }
+    if (slow) {
         float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[1][0], sacc[1][1]);
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) {  // two chains of three-input max
+        for (int r = 2; r < 16; r += 2) {
             m0 = fmaxf(m0, fmaxf(sacc[0][r], sacc[0][r + 1]));
             m1 = fmaxf(m1, fmaxf(sacc[1][r], sacc[1][r + 1]));
         }
-        mx = fmaxf(m0, m1);
-    }
-    mx = pair_max(mx);
-    const float m_tile = mx * scale_log2;
-    const float m_new = (m_tile > st.m_run + 8.f) ? m_tile : st.m_run;
-    const float alpha = (m_new == st.m_run) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-    if (__ballot(alpha != 1.f)) {
+        const float m_tile = pair_max(fmaxf(m0, m1)) * scale_log2;
+        const float m_new = fmaxf(st.m_run, m_tile);
+        const float alpha = (m_new == st.m_run) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+        if (__ballot(alpha != 1.f)) {
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
+            for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
+        }
+        st.l_run *= alpha;
+        st.m_run = m_new;
+        probs((m_new == -INFINITY) ? 0.f : -m_new);
     }
-    st.l_run *= alpha;
-    st.m_run = m_new;
-    const float neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
-
-    float lsum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int m2 = 0; m2 < 2; ++m2) {
-            bf16x8 pop;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                pop[j] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
-            // row sum of the bf16 probabilities that enter PV, two per dot2
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 0, 1), kOnes2, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 2, 3), kOnes2, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 4, 5), kOnes2, lsum, false);
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pop, pop, 6, 7), kOnes2, lsum, false);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
                 s16x4 half[2];
@@ -366,7 +384,7 @@ __device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&
                         (__attribute__((address_space(3))) s16x4 *)(addr));
                 }
                 const s16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                st.oacc[db] = mfma32(__builtin_bit_cast(bf16x8, both), pop, st.oacc[db]);
+                st.oacc[db] = mfma32(__builtin_bit_cast(bf16x8, both), pop[kb * 2 + m2], st.oacc[db]);
             }
         }
     st.l_run += lsum;

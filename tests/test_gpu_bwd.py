@@ -8,7 +8,7 @@ gradients in double from the same seeded q, k, v, dO.  Bars:
   - bf16: max |gpu - oracle| <= 2e-2 * max(1, max |oracle|) and
           mean |gpu - oracle| <= 2e-3 * max(1, mean |oracle|).
     Every gradient term carries at most two bf16 roundings (P or dS as an
-    MFMA operand, each <= 2^-9 relative) on top of fp32 accumulation, and the
+    MFMA operand, each <= 2^-8 relative: bf16 carries 8 significant bits) on top of fp32 accumulation, and the
     output is rounded once more; D = dO . o uses the bf16 forward output.
     The normalised bar is the forward's (2e-2 / 2e-3) scaled by the size of
     the gradient, since dK and dV sum over many queries and heads.

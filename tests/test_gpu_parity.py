@@ -5,11 +5,11 @@ the oracle receives a host copy of the very same tensors.  Bars:
   - expansion gather and decode cache append: bit-exact;
   - bf16 attention: max |gpu - oracle| <= 2e-2 and mean <= 2e-3;
   - float32 attention: max |gpu - oracle| <= 1e-4;
-  - lse: max abs <= 2.5e-3 for bf16 (the softmax denominator is summed from
-    the bf16-rounded probabilities that enter the PV product; each carries a
-    relative rounding error <= 2^-9, so ln of their sum is within 2^-9 =
-    1.95e-3 of ln of the exact sum, plus ~1e-4 for fp32 scores and exp2),
-    1e-4 for float32.
+  - lse: max abs <= 4e-3 for bf16 (the softmax denominator is summed from
+    the bf16-rounded probabilities that enter the PV product; bf16 carries 8
+    significant bits, so each has a relative rounding error <= 2^-8 and ln of
+    their sum is within ln(1 + 2^-8) = 3.9e-3 of ln of the exact sum, plus
+    ~1e-4 for fp32 scores and exp2), 1e-4 for float32.
 Small shapes are compared on every output; the full workload sizes are
 compared on sampled rows (stream boundaries, window edges, first/last tokens,
 tile edges, random interior rows).
@@ -49,7 +49,7 @@ def check_bf16(got, want, what, max_abs=2e-2, mean_abs=2e-3):
     assert diff.mean() <= mean_abs, f"{what}: mean abs {diff.mean():.3e} > {mean_abs}"
 
 
-LSE_TOL_BF16 = 2.5e-3
+LSE_TOL_BF16 = 4e-3
 
 
 def check_f32(got, want, what, tol=1e-4):
@@ -300,3 +300,19 @@ def test_decode_deterministic_and_guarded():
         torch.cuda.synchronize()
         assert torch.equal(o1, o2)
         assert (buf[:guard] == 3.0).all() and (buf[guard + q.numel():] == 3.0).all()
+
+
+@pytest.mark.parametrize("mode", [INTRA, CROSS])
+def test_fwd_bf16_extreme_score_growth(mode):
+    """Scores spanning hundreds of log2 units (scale 1, |q| ~ 8): the running
+    max must be raised mid-row (probabilities against a stale max overflow
+    fp32), exercising the rescale path of every kernel."""
+    B, L, n, Hq, Hkv, d = 1, 300, 2, 4, 2, 128
+    q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.bfloat16, DEV)
+    q = (q.float() * 8.0).to(torch.bfloat16)
+    o, lse = hd.sfa_fwd(q, k, v, n, mode, 0, 1.0, return_lse=True)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), n, mode, 0, 1.0)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    check_bf16(o, want, f"extreme mode={mode}")
+    # lse is ~1e3 here: its bar is relative to fp32 score rounding
+    check_f32(lse, wlse, "lse", tol=LSE_TOL_BF16 + 1e-6 * float(np.abs(wlse).max()))

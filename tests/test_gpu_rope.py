@@ -114,7 +114,7 @@ def test_fwd_rope_vs_oracle(shape, mode, window, dtype):
     if dtype == torch.float32:
         assert err.max() <= 1e-4 and lerr.max() <= 1e-4
     else:
-        assert err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 2.5e-3
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3 and lerr.max() <= 4e-3
 
 
 def test_fwd_rope_in_place_and_final_layout():
