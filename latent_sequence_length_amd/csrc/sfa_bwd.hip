@@ -469,6 +469,200 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(BwdArgs p, int HG, 
     if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + pos * qrs + (int64_t)h * D, dq, p.scale, hi);
 }
 
+// 3'. dQ at head dim 128 on the forward's d=128 structure: a workgroup is 8
+// waves (HG heads of one GQA group x 8/HG blocks of 32 queries) sharing 64-key
+// K/V tiles brought in by direct-to-LDS 16-byte copies (global_load_lds),
+// double-buffered, one barrier per tile.  K and V rows are 256 B with the
+// 16-byte chunk index XOR-swizzled by swzv(row): conflict-free both for the
+// row reads of S^T = K Q^T and dP^T = V dO^T (A operands: 16 rows, one chunk)
+// and for the transposed K reads of dQ^T += K^T dS^T (4 rows x 4 chunks per
+// 32 lanes).  Per tile and wave (lane = query, registers = keys):
+//   S^T, dP^T [64 keys x 32 queries]
+//   P^T = exp2(scale*log2e * S^T - lse*log2e),  dS^T = P^T (dP^T - D)
+//   dQ^T += K^T dS^T, the dS^T accumulators serving directly as B operand.
+constexpr int DQ_NW = 8;  // waves per workgroup of the head-dim-128 dQ kernel
+
+template <bool GQ>
+__global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, int HG, int TB, int nqblk) {
+    constexpr int D = 128, KT = 64, QW = 32;
+    constexpr int TILE = KT * D * 2;  // 16 KB per K or V tile
+    __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K | V, even tiles
+    __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];  // K | V, odd tiles
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int g = p.Hq / p.Hkv, ngrp = g / HG;
+
+    // workgroup -> (query block, group), longest blocks first, balanced over
+    // the 8 XCDs as in the forward
+    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
+    const int nwg = nrest * nqblk;
+    const int bid = blockIdx.x;
+    int lid = bid;
+    if (nwg % 8 == 0) {
+        const int x = bid % 8, j = bid / 8;
+        if (nrest % 8 == 0) {
+            lid = x * (nwg / 8) + j;
+        } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
+            const int r = 8 / nrest;
+            lid = (x / r) * nqblk + j * r + x % r;
+        }
+    }
+    const int qblk = nqblk - 1 - lid % nqblk;
+    int rest = lid / nqblk;
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int hgrp = rest % ngrp; rest /= ngrp;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+
+    const int QB = QW * TB;
+    const int q0 = qblk * QB;
+    const int h = kvh * g + hgrp * HG + wave % HG;
+    const int qw0 = q0 + (wave / HG) * QW;
+    const int myq = qw0 + l32;
+    const bool qvalid = myq < p.Lq;
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    const int mylim = myq * qmul + qadd;            // last key this query may see
+    const int lim0 = qw0 * qmul + qadd;             // ... for the wave's first query
+    const int lim1 = (qw0 + QW - 1) * qmul + qadd;  // ... and its last
+
+    const int64_t qrs = (int64_t)p.Hq * D, krs = (int64_t)p.Hkv * D;
+    const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;  // key element 0
+    const bf16 *kg = static_cast<const bf16 *>(p.k) + (int64_t)kvh * D;
+    const bf16 *vg = static_cast<const bf16 *>(p.v) + (int64_t)kvh * D;
+
+    const int kend = min((min(q0 + QB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
+    const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
+    const int tfirst = kbeg & ~(KT - 1);
+    const int ntiles = (kend - tfirst + KT - 1) / KT;
+
+    // copy-in: wave w moves rows (w*PER + i)*4 + lane/16 of each tile, lane l
+    // filling physical chunk l%16 with logical chunk (l%16) ^ swzv(row); rows
+    // past the end of the sub-sequence re-read its last row (masked later)
+    const int rstride = p.stride * (int)krs;
+    constexpr int PER = 16 / DQ_NW;
+    int lrow[PER], lchunk[PER];
+    unsigned boff[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        lrow[i] = (wave * PER + i) * 4 + (lane >> 4);
+        lchunk[i] = ((lane & 15) ^ swzv(lrow[i])) * 8;
+        boff[i] = (unsigned)(lrow[i] * rstride + lchunk[i]) * 2u;
+    }
+    auto issue = [&](int t0, char *dst) {
+        const int64_t tbase = (bpos + (int64_t)t0 * p.stride) * krs;
+        const bf16 *kt = kg + tbase, *vt = vg + tbase;
+        const int rmax = p.Lsub - 1 - t0;
+        unsigned bo[PER];
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            bo[i] = (rmax < KT - 1) ? (unsigned)(min(lrow[i], rmax) * rstride + lchunk[i]) * 2u : boff[i];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int s0 = (wave * PER + i) * 64;
+            lds_dma16_s(kt, bo[i], lds_addr(dst + s0 * 16));
+            lds_dma16_s(vt, bo[i], lds_addr(dst + TILE + s0 * 16));
+        }
+    };
+    if (ntiles > 0) issue(tfirst, buf0);
+
+    // B operands Q^T and dO^T: lane = query, k-slots = dims 16*ks + 8*hi .. +7
+    const int64_t qrow = (int64_t)b * p.qrows + (int64_t)sub * p.qsub + (int64_t)(qvalid ? myq : 0) * p.qstride;
+    bf16x8 qf[D / 16], gf[D / 16];
+    {
+        const bf16 *qp = static_cast<const bf16 *>(p.q) + qrow * qrs + (int64_t)h * D + 8 * hi;
+        const bf16 *gp = static_cast<const bf16 *>(p.dout) + qrow * qrs + (int64_t)h * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + 16 * ks);
+            const bf16x8 y = *reinterpret_cast<const bf16x8 *>(gp + 16 * ks);
+            qf[ks] = qvalid ? x : bf16x8{};
+            gf[ks] = qvalid ? y : bf16x8{};
+        }
+    }
+    const float c2 = p.scale * kLog2e;
+    const float lse2 = qvalid ? p.lse[row_stat(p, b, h, qrow)] * kLog2e : 0.f;
+    const float Dq = qvalid ? p.drow[row_stat(p, b, h, qrow)] : 0.f;
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
+
+    const int rsw = swzv(l32);  // swzv(32*kb + l32) == swzv(l32)
+    auto tile = [&](const char *cur, int t0) {
+        const bool active = (t0 <= lim1) && (p.weff == 0 || t0 + KT - 1 > lim0 - p.weff);
+        if (!active) return;
+        const bool need_mask = (t0 + KT - 1 > lim0) || (t0 + KT > p.Lsub) || (p.weff != 0 && t0 <= lim1 - p.weff);
+        const char *kbuf = cur, *vbuf = cur + TILE;
+        f32x16 s[2], dp[2];
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = dp[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int off = (kb * 32 + l32) * 256 + (((2 * ks + hi) ^ rsw) << 4);
+                s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kbuf + off), qf[ks], s[kb]);
+                dp[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(vbuf + off), gf[ks], dp[kb]);
+            }
+        __builtin_amdgcn_s_setprio(0);
+        if (need_mask) {  // visible <=> lo <= key <= hi_key, one unsigned compare
+            const int lo = p.weff ? mylim - p.weff + 1 : 0;
+            const unsigned span = (unsigned)(min(mylim, p.Lsub - 1) - lo);
+            const int base = t0 + 4 * hi - lo;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const unsigned u = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
+                    s[kb][r] = (u <= span) ? s[kb][r] : -INFINITY;
+                }
+        }
+        // register r of block kb holds key t0 + 32*kb + 8*(r/4) + 4*hi + r%4
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                bf16x8 dsop;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int r = 8 * m2 + j;
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2));
+                    dsop[j] = (bf16)(pr * (dp[kb][r] - Dq));
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    s16x4 half[2];
+#pragma unroll
+                    for (int jh = 0; jh < 2; ++jh) {
+                        const int row = kb * 32 + 16 * m2 + 8 * jh + 4 * hi + (l16 >> 2);
+                        const int dim = db * 32 + 16 * g2 + 4 * (l16 & 3);
+                        half[jh] = lds_read_tr16(kbuf + row * 256 + (((dim >> 3) ^ swzv(row)) << 4) +
+                                                 ((dim >> 2) & 1) * 8);
+                    }
+                    const s16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    dq[db] = mfma32(__builtin_bit_cast(bf16x8, both), dsop, dq[db]);
+                }
+            }
+    };
+
+    for (int it = 0; it < ntiles; it += 2) {
+        const int t0 = tfirst + it * KT;
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of tile it have landed
+        __syncthreads();                // ... and every wave's; tile it-1 fully consumed
+        if (it + 1 < ntiles) issue(t0 + KT, buf1);
+        tile(buf0, t0);
+        if (it + 1 < ntiles) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (it + 2 < ntiles) issue(t0 + 2 * KT, buf0);
+            tile(buf1, t0 + KT);
+        }
+    }
+    if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + qrow * qrs + (int64_t)h * D, dq, p.scale, hi);
+}
+
 // dK and dV rows that no key sub-sequence covers (the other streams of a
 // final-stream intra layer: position t is covered iff (t - kbase) mod stride
 // < nsub) receive no gradient: write zeros, 16 bytes per thread.
@@ -520,7 +714,17 @@ hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)kgrid), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GQ>), dim3((unsigned)qgrid), dim3(256), 0, st, a, HG, TB, nqblk);
+    // 32-bit per-lane copy offsets of the d=128 dQ kernel: rows 0..63 of a tile
+    if (D == 128 && (int64_t)64 * a.stride * a.Hkv * D * 2 < ((int64_t)1 << 32)) {
+        const int TB2 = DQ_NW / HG;
+        const int nqblk2 = (a.Lq + 32 * TB2 - 1) / (32 * TB2);
+        const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
+        if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_dq_d128_kernel<GQ>), dim3((unsigned)grid2), dim3(64 * DQ_NW), 0, st, a, HG, TB2,
+                           nqblk2);
+    } else {
+        hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GQ>), dim3((unsigned)qgrid), dim3(256), 0, st, a, HG, TB, nqblk);
+    }
     return hipGetLastError();
 }
 
