@@ -69,7 +69,7 @@ def _configure(lib):
     lib.oracle_sfa_decode.argtypes = [P, P, P, P, P, I, P, I, I, I, I, I, I, I, I64, D, P]
     lib.oracle_decode_append.argtypes = [P, P, P, I, I, I, I, I, I64]
     lib.oracle_sfa_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, I64, D, P, P, P, I64, P, P, I64, P, P]
-    lib.oracle_rope.argtypes = [P, I, I, I, I, I, P, I64, D, P]
+    lib.oracle_rope.argtypes = [P, I, I, I, I, I, P, I64, I64, I64, D, P]
     for f in (lib.oracle_expand_embed, lib.oracle_visible, lib.oracle_sfa_rows,
               lib.oracle_sfa_fwd, lib.oracle_sfa_decode, lib.oracle_decode_append, lib.oracle_sfa_bwd_rows,
               lib.oracle_rope):
@@ -355,9 +355,10 @@ def sfa_final_bwd(qf, k, v, doutf, n, mode, window=0, scale=0.0):
     return dq.reshape(B, L, Hq, d), dk.reshape(B, nL, Hkv, d), dv.reshape(B, nL, Hkv, d)
 
 
-def rope(x, theta=10000.0, pos_base=None, pos_mul=0):
-    """Rotary embedding of x [B, T, H, d] at positions t + pos_mul*pos_base[b]
-    ("rotate half" pairing c <-> c + d/2); returns float64 [B, T, H, d]."""
+def rope(x, theta=10000.0, pos_base=None, pos_mul=0, t_mul=1, t_add=0):
+    """Rotary embedding of x [B, T, H, d] at positions
+    t*t_mul + t_add + pos_mul*pos_base[b] ("rotate half" pairing c <-> c + d/2);
+    returns float64 [B, T, H, d]."""
     xb, dt = _buf(x)
     B, T, H, d = xb.shape
     out = np.empty((B, T, H, d), dtype=np.float64)
@@ -365,7 +366,7 @@ def rope(x, theta=10000.0, pos_base=None, pos_mul=0):
     if pos_base is not None:
         pb = np.ascontiguousarray(np.asarray(pos_base, dtype=np.int32))
     rc = _load().oracle_rope(_p(xb), dt, B, T, H, d, _p(pb) if pb is not None else None, int(pos_mul),
-                             float(theta), _p(out))
+                             int(t_mul), int(t_add), float(theta), _p(out))
     if rc:
         raise ValueError("oracle_rope rejected its arguments")
     return out

@@ -511,18 +511,23 @@ int oracle_sfa_final_bwd_rows(const void *qf, const void *k, const void *v, cons
  *   out[c]     = x[c]     cos(t f_c) - x[c + h] sin(t f_c)
  *   out[c + h] = x[c + h] cos(t f_c) + x[c]     sin(t f_c)
  * x [B][T][H][d] (float32 or bf16 bits); out [B][T][H][d] double.  The
- * position of row (b, t) is t + pos_mul * pos_base[b] (pos_base may be NULL):
- * a prefill passes NULL; a decode step passes the cached token counts with
- * pos_mul = n, so stream s of the new token sits at len*n + s.
+ * position of row (b, t) is t*t_mul + t_add + pos_mul * pos_base[b]
+ * (pos_base may be NULL): a prefill passes NULL with t_mul = 1, t_add = 0; the
+ * final-stream rows of a KV-mirror layer (row i is expanded position
+ * i*n + n-1) pass t_mul = n, t_add = n-1; a decode step passes the cached
+ * token counts with pos_mul = n, so stream s of the new token sits at
+ * len*n + s (t_add = n-1 for the final stream's row alone).
  * Returns 0 or -1.
  * ------------------------------------------------------------------------- */
 int oracle_rope(const void *x, int dtype, int B, int T, int H, int d, const int32_t *pos_base,
-                int64_t pos_mul, double theta, double *out) {
-    if (B < 1 || T < 1 || H < 1 || d < 2 || d % 2 || theta <= 0.0 || pos_mul < 0) return -1;
+                int64_t pos_mul, int64_t t_mul, int64_t t_add, double theta, double *out) {
+    if (B < 1 || T < 1 || H < 1 || d < 2 || d % 2 || theta <= 0.0 || pos_mul < 0 || t_mul < 0 || t_add < 0)
+        return -1;
     const int h = d / 2;
     for (int64_t b = 0; b < B; ++b)
         for (int64_t t = 0; t < T; ++t) {
-            const double pos = (double)t + (pos_base ? (double)pos_mul * (double)pos_base[b] : 0.0);
+            const double pos = (double)(t * t_mul + t_add) +
+                               (pos_base ? (double)pos_mul * (double)pos_base[b] : 0.0);
             for (int64_t hh = 0; hh < H; ++hh) {
                 const int64_t row = ((b * T + t) * H + hh) * d;
                 for (int c = 0; c < h; ++c) {

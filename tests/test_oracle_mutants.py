@@ -60,8 +60,10 @@ MUTANTS = [
     ("rope frequency exponent off by one", "const double f = pow(theta, -2.0 * c / d);",
      "const double f = pow(theta, -2.0 * (c + 1) / d);",
      [pins.test_rope_matches_transformers_rotate_half, pins.test_rope_golden_d4]),
-    ("rope decode position ignores the stream", "const double pos = (double)t + (pos_base ?",
-     "const double pos = (double)0 * t + (pos_base ?", [pins.test_rope_decode_positions]),
+    ("rope decode position ignores the stream", "const double pos = (double)(t * t_mul + t_add) +",
+     "const double pos = (double)(0 * t * t_mul + t_add) +", [pins.test_rope_decode_positions]),
+    ("rope row offset dropped", "const double pos = (double)(t * t_mul + t_add) +",
+     "const double pos = (double)(t * t_mul) +", [pins.test_rope_final_stream_and_final_decode_positions]),
     ("final query placed at stream 0", "int64_t t = i * n + (n - 1);   /* the final stream's expanded position */",
      "int64_t t = i * n;   /* the final stream's expanded position */",
      [lambda o: pins.test_final_matches_sdpa_with_onebased_rows(o, CROSS, 0), pins.test_final_closed_forms]),

@@ -729,3 +729,22 @@ def test_decode_final_equals_final_prefill_rows(oracle, mode, W):
         qseq[0, ln] = qf[b, 0]
         of, _ = oracle.sfa_final(qseq, kseq, vseq, n, mode, W)
         np.testing.assert_allclose(o[b, 0], of[0, ln], rtol=0, atol=1e-14)
+
+
+def test_rope_final_stream_and_final_decode_positions(oracle):
+    """t_mul / t_add place compact final-stream rows (row i at i*n + n-1) and
+    the final stream's decode row (len*n + n-1): equal to those rows of the
+    plain prefill rotation."""
+    n, H, d, L = 3, 2, 16, 6
+    x = _rand((2, n * L, H, d), 56)
+    full = oracle.rope(x, 10000.0)
+    xf = x[:, n - 1::n].contiguous()
+    got = oracle.rope(xf, 10000.0, t_mul=n, t_add=n - 1)
+    np.testing.assert_allclose(got, full[:, n - 1::n], rtol=0, atol=1e-13)
+    lens = [4, 0]
+    q1 = _rand((2, 1, H, d), 57)
+    dec = oracle.rope(q1, 10000.0, pos_base=lens, pos_mul=n, t_add=n - 1)
+    for b, ln in enumerate(lens):
+        seq = torch.zeros(1, (ln + 1) * n, H, d)
+        seq[0, ln * n + n - 1] = q1[b, 0]
+        np.testing.assert_allclose(dec[b, 0], oracle.rope(seq, 10000.0)[0, ln * n + n - 1], rtol=0, atol=1e-13)
