@@ -98,17 +98,22 @@ hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, 
  * h = d/2, f_c = theta^(-2c/d):
  *   out[..][c]     = x[c] cos(p f_c) - x[c+h] sin(p f_c)
  *   out[..][c + h] = x[c+h] cos(p f_c) + x[c] sin(p f_c)
- * with position p = t + pos_mul * pos_base[b] for row (b, t).
+ * with position p = t*t_mul + t_add + pos_mul * pos_base[b] for row (b, t).
  *   x, out    [B][T][H][d] (dtype dt); out may equal x (in place)
- *   pos_base  device int32 [B] or NULL (0): prefill of the expanded sequence
- *             passes NULL (p = t); a decode step passes q or k_new as
- *             [B][n][H][d] with pos_base = cache_len and pos_mul = n, so
- *             stream s of the new token gets p = len*n + s
- * Apply it to q and k before hd_sfa_fwd / hd_sfa_decode.  Requires B, T, H >= 1,
- * d in {32, 64, 128}, theta > 0, pos_mul >= 0.
+ *   pos_base  device int32 [B] or NULL (0)
+ * The rows the library's entry points take:
+ *   prefill q, k [B][n*L][H][d]:           pos_base NULL, t_mul 1, t_add 0 (p = t)
+ *   final-stream q [B][L][H][d] (KV-mirror): pos_base NULL, t_mul n, t_add n-1
+ *                                           (row i is position i*n + n-1)
+ *   decode q, k_new [B][n][H][d]:          pos_base = cache_len, pos_mul n,
+ *                                           t_mul 1, t_add 0 (p = len*n + s)
+ *   final-stream decode q [B][1][H][d]:     pos_base = cache_len, pos_mul n,
+ *                                           t_add n-1 (p = len*n + n-1)
+ * Apply it to q and k before the attention call.  Requires B, T, H >= 1,
+ * d in {32, 64, 128}, theta > 0, pos_mul, t_mul, t_add >= 0.
  */
 hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,
-                  float theta, hd_dtype dt, void *stream);
+                  int64_t t_mul, int64_t t_add, float theta, hd_dtype dt, void *stream);
 
 /*
  * Stream-Factorized Attention prefill ("Stream-Factorized Attention", index

@@ -201,7 +201,7 @@ hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, 
         return fail(HD_ERR_INVALID, "lse is not 4-byte aligned");
     hipStream_t st = static_cast<hipStream_t>(stream);
     hd::RopeArgs ra{};  // k -> k_rot at positions 0 .. n*L-1
-    ra.x = k; ra.out = k_rot; ra.pos_base = nullptr; ra.pos_mul = 0;
+    ra.x = k; ra.out = k_rot; ra.pos_base = nullptr; ra.pos_mul = 0; ra.t_mul = 1; ra.t_add = 0;
     ra.B = B; ra.T = n * L; ra.H = Hkv; ra.d = d;
     rope_freqs(ra.freq_turns, d, theta);
     hipError_t e = hd::launch_rope(ra, dt == HD_BF16, st);
@@ -218,18 +218,20 @@ hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, 
 }
 
 hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const int32_t *pos_base, int64_t pos_mul,
-                  float theta, hd_dtype dt, void *stream) {
+                  int64_t t_mul, int64_t t_add, float theta, hd_dtype dt, void *stream) {
     if (B < 1 || T < 1 || H < 1) return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d T=%d H=%d)", B, T, H);
     if (d != 32 && d != 64 && d != 128) return fail(HD_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
     if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
     if (!(theta > 0.f) || !std::isfinite(theta)) return fail(HD_ERR_INVALID, "theta=%g must be > 0", (double)theta);
-    if (pos_mul < 0) return fail(HD_ERR_INVALID, "pos_mul=%lld < 0", (long long)pos_mul);
+    if (pos_mul < 0 || t_mul < 0 || t_add < 0)
+        return fail(HD_ERR_INVALID, "pos_mul=%lld, t_mul=%lld, t_add=%lld must be >= 0", (long long)pos_mul,
+                    (long long)t_mul, (long long)t_add);
     HD_TRY(check_ptr(x, "x"));
     HD_TRY(check_ptr(out, "out"));
     if (pos_base != nullptr && (reinterpret_cast<uintptr_t>(pos_base) & 3u))
         return fail(HD_ERR_INVALID, "pos_base is not 4-byte aligned");
     hd::RopeArgs a{};
-    a.x = x; a.out = out; a.pos_base = pos_base; a.pos_mul = pos_mul;
+    a.x = x; a.out = out; a.pos_base = pos_base; a.pos_mul = pos_mul; a.t_mul = t_mul; a.t_add = t_add;
     a.B = B; a.T = T; a.H = H; a.d = d;
     rope_freqs(a.freq_turns, d, theta);
     return device_status(hd::launch_rope(a, dt == HD_BF16, static_cast<hipStream_t>(stream)), "rope launch");

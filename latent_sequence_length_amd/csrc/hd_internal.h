@@ -85,12 +85,13 @@ hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st);
 
 // ---------------------------------------------------------------------------
-// Rotary embedding of x [B][T][H][d] at positions t + pos_mul * pos_base[b].
+// Rotary embedding of x [B][T][H][d] at positions
+// t*t_mul + t_add + pos_mul * pos_base[b].
 struct RopeArgs {
     const void *x;
     void *out;                // may equal x
     const int32_t *pos_base;  // device [B] or NULL
-    int64_t pos_mul;
+    int64_t pos_mul, t_mul, t_add;
     int B, T, H, d;
     double freq_turns[64];    // theta^(-2c/d) / (2 pi), c < d/2
 };

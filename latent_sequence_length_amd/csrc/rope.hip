@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void rope_kernel(RopeArgs a) {
     const unsigned bt = idx / (unsigned)nch;
     const int c0 = (int)(idx - bt * (unsigned)nch) * 8;
     const unsigned b = bt / (unsigned)a.T, t = bt - b * (unsigned)a.T;
-    const int64_t pos = (int64_t)t + (a.pos_base != nullptr ? a.pos_mul * (int64_t)a.pos_base[b] : 0);
+    const int64_t pos = (int64_t)t * a.t_mul + a.t_add + (a.pos_base != nullptr ? a.pos_mul * (int64_t)a.pos_base[b] : 0);
     float cs[8], sn[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

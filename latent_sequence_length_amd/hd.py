@@ -51,7 +51,7 @@ def load():
     lib.hd_sfa_bwd_final_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.hd_sfa_bwd_final_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd_final.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
-    lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, F, I, P]
+    lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, I64, I64, F, I, P]
     for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_fwd_rope, lib.hd_sfa_decode,
               lib.hd_sfa_decode_final, lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
         f.restype = ctypes.c_int
@@ -227,8 +227,9 @@ def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=
     return o
 
 
-def hd_rope(x, out, theta=10000.0, pos_base=None, pos_mul=0):
-    """Rotary embedding of x [B, T, H, d] at positions t + pos_mul*pos_base[b] into out (may be x)."""
+def hd_rope(x, out, theta=10000.0, pos_base=None, pos_mul=0, t_mul=1, t_add=0):
+    """Rotary embedding of x [B, T, H, d] at positions
+    t*t_mul + t_add + pos_mul*pos_base[b] into out (may be x)."""
     B, T, H, d = x.shape
     if out.shape != x.shape or out.dtype != x.dtype:
         raise ValueError("out must match x in shape and dtype")
@@ -237,8 +238,8 @@ def hd_rope(x, out, theta=10000.0, pos_base=None, pos_mul=0):
         if pos_base.shape != (B,):
             raise ValueError("pos_base must be [B]")
         pb = _dev(pos_base, "pos_base", torch.int32)
-    _check(load().hd_rope(_dev(x, "x"), _dev(out, "out"), B, T, H, d, pb, int(pos_mul), float(theta),
-                          _dtype_code(x), _stream(x)))
+    _check(load().hd_rope(_dev(x, "x"), _dev(out, "out"), B, T, H, d, pb, int(pos_mul), int(t_mul), int(t_add),
+                          float(theta), _dtype_code(x), _stream(x)))
     return out
 
 
@@ -362,5 +363,5 @@ def sfa_bwd_final(q, k, v, o, dout, lse, n, mode, window=0, scale=0.0):
     return hd_sfa_bwd_final(q, k, v, o, dout, lse, dq, dk, dv, n, mode, window, scale)
 
 
-def rope(x, theta=10000.0, pos_base=None, pos_mul=0):
-    return hd_rope(x, torch.empty_like(x), theta, pos_base, pos_mul)
+def rope(x, theta=10000.0, pos_base=None, pos_mul=0, t_mul=1, t_add=0):
+    return hd_rope(x, torch.empty_like(x), theta, pos_base, pos_mul, t_mul, t_add)

@@ -32,7 +32,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     assert declared_symbols() == sorted([
-        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_fwd_rope", "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
+        "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_fwd_rope",
+        "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_bwd_final_workspace_bytes", "hd_sfa_bwd_final",
         "hd_sfa_decode_workspace_bytes", "hd_sfa_decode", "hd_sfa_decode_final",
         "hd_status_string", "hd_last_error", "hd_version"])
@@ -183,10 +184,12 @@ def test_bwd_workspace_size(lib):
 
 def test_rope_validation(lib):
     f = lib.hd_rope
-    ok = dict(x=FAKE, out=FAKE, B=1, T=8, H=2, d=64, pos_base=None, pos_mul=0, theta=10000.0, dt=0, stream=None)
+    ok = dict(x=FAKE, out=FAKE, B=1, T=8, H=2, d=64, pos_base=None, pos_mul=0, t_mul=1, t_add=0, theta=10000.0,
+              dt=0, stream=None)
     for kw, code in [(dict(B=0), hd.HD_ERR_INVALID), (dict(T=0), hd.HD_ERR_INVALID), (dict(d=48), hd.HD_ERR_UNSUPPORTED),
                      (dict(theta=0.0), hd.HD_ERR_INVALID), (dict(theta=-1.0), hd.HD_ERR_INVALID),
-                     (dict(pos_mul=-1), hd.HD_ERR_INVALID), (dict(x=None), hd.HD_ERR_INVALID),
+                     (dict(pos_mul=-1), hd.HD_ERR_INVALID), (dict(t_mul=-1), hd.HD_ERR_INVALID),
+                     (dict(t_add=-3), hd.HD_ERR_INVALID), (dict(x=None), hd.HD_ERR_INVALID),
                      (dict(out=FAKE + 2), hd.HD_ERR_INVALID), (dict(pos_base=FAKE + 2), hd.HD_ERR_INVALID),
                      (dict(dt=9), hd.HD_ERR_UNSUPPORTED)]:
         a = dict(ok)

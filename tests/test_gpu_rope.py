@@ -146,3 +146,22 @@ def test_fwd_rope_full_size_sampled():
     err = np.abs(got - want)
     sys.__stdout__.write(f"  rows max {err.max():.3e} mean {err.mean():.3e}\n")
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+def test_rope_final_stream_rows_and_final_decode():
+    """Compact final-stream rows (t_mul = n, t_add = n-1) and the final
+    stream's decode row (pos_base = len, pos_mul = n, t_add = n-1) against the
+    oracle, and the final-stream rows equal rows n-1, 2n-1, ... of the plain
+    prefill rotation bit for bit (same angles, same kernel)."""
+    n, L, H, d = 4, 300, 8, 128
+    x = synth.normal((2, n * L, H, d), 33, torch.bfloat16, DEV)
+    full = hd.rope(x, 10000.0)
+    xf = x[:, n - 1::n].contiguous()
+    fin = hd.rope(xf, 10000.0, t_mul=n, t_add=n - 1)
+    assert torch.equal(fin, full[:, n - 1::n])
+    check_rope(fin, xf, oracle.rope(xf.cpu(), 10000.0, t_mul=n, t_add=n - 1), 2.0 ** -8 + 1e-6)
+    lens = torch.tensor([8192, 0, 17], dtype=torch.int32, device=DEV)
+    q1 = synth.normal((3, 1, H, d), 34, torch.bfloat16, DEV)
+    got = hd.rope(q1, 10000.0, lens, n, t_add=n - 1)
+    check_rope(got, q1, oracle.rope(q1.cpu(), 10000.0, pos_base=lens.cpu().numpy(), pos_mul=n, t_add=n - 1),
+               2.0 ** -8 + 1e-6)
