@@ -17,7 +17,7 @@
 //
 // Three launches, no atomics, every output element written once:
 //   1. D_i = dO_i . O_i for every query row (fp32, into the workspace);
-//   2. dK, dV: a workgroup owns 128 keys of one (batch, kv head, sub-sequence)
+//   2. dK, dV: a workgroup owns 256 keys of one (batch, kv head, sub-sequence)
 //      and walks the query tiles (all heads of the group) that see them,
 //      staging the tiles of up to four heads per barrier;
 //   3. dQ: a wave owns 32 queries of one head and walks the key tiles they see
@@ -30,7 +30,7 @@ namespace {
 
 constexpr int BKT = 64;   // keys per tile (dQ kernel)
 constexpr int BQT = 32;   // queries per tile (dK/dV kernel)
-constexpr int BKW = 128;  // keys per workgroup (dK/dV kernel)
+constexpr int BKW = 256;  // keys per workgroup (dK/dV kernel)
 
 // ---------------------------------------------------------------------------
 // 1. D = dO . O per query row; 16 lanes per row, fp32.
@@ -199,19 +199,19 @@ __device__ __forceinline__ bf16x8 read_rows_tr(const char *tile, int row0, int c
 
 // Copy `rows` rows of D bf16 (global row stride `rstride` elements, first row
 // `base`) into a padded LDS tile; rows at or past `nvalid` are zero.
-template <int D, int ROWS>
+template <int D, int ROWS, int NT = 256>
 __device__ __forceinline__ void stage_rows(char *tile, const bf16 *base, int64_t rstride, int nvalid) {
-    constexpr int CH = D / 8, PITCH = 2 * D + 16, PER = (ROWS * CH + 255) / 256;
+    constexpr int CH = D / 8, PITCH = 2 * D + 16, PER = (ROWS * CH + NT - 1) / NT;
     uint4 x[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {  // all loads first, then all stores
-        const int c = threadIdx.x + 256 * u, r = c / CH, cc = c - r * CH;
+        const int c = threadIdx.x + NT * u, r = c / CH, cc = c - r * CH;
         x[u] = uint4{0, 0, 0, 0};
         if (c < ROWS * CH && r < nvalid) x[u] = *reinterpret_cast<const uint4 *>(base + r * rstride + cc * 8);
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int c = threadIdx.x + 256 * u, r = c / CH, cc = c - r * CH;
+        const int c = threadIdx.x + NT * u, r = c / CH, cc = c - r * CH;
         if (c < ROWS * CH) *reinterpret_cast<uint4 *>(tile + r * PITCH + cc * 16) = x[u];
     }
 }
@@ -231,14 +231,16 @@ __device__ __forceinline__ void store_rows(bf16 *out, const f32x16 (&acc)[D / 32
         }
 }
 
-// 2. dK, dV.  Workgroup = 4 waves x 32 keys of one (b, kv head, sub); per
-// query tile (32 queries of one head of the group):
+// 2. dK, dV.  Workgroup = 8 waves x 32 keys of one (b, kv head, sub), two
+// waves per SIMD and one workgroup per CU, so every staged query tile serves
+// 256 keys (half the L2-to-LDS traffic of a 4-wave group); per query tile
+// (32 queries of one head of the group):
 //   S = Q K^T, dP = dO V^T      [32 q x 32 k]: lane = key, registers = queries
 //   P = exp(S*scale - lse), dS = P (dP - D)
 //   dV^T += dO^T P, dK^T += Q^T dS   [D x 32 k]
 // GQ: the query map is not the identity (final-stream queries).
 template <int D, bool GQ>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     constexpr int PITCH = 2 * D + 16;
     constexpr int HS = 4;  // heads of the group staged per round
     __shared__ __attribute__((aligned(16))) char Qs[HS][BQT * PITCH];
@@ -293,9 +295,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16_kernel(BwdArgs p) {
             const int64_t qpos0 = q_row(p, b, sub, i0);
             for (int hh = 0; hh < nh; ++hh) {
                 const int h = kvh * g + h0 + hh;
-                stage_rows<D, BQT>(Qs[hh], static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D,
+                stage_rows<D, BQT, 512>(Qs[hh], static_cast<const bf16 *>(p.q) + qpos0 * qrs + (int64_t)h * D,
                                    p.qstride * qrs, nvalid);
-                stage_rows<D, BQT>(Gs[hh], static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D,
+                stage_rows<D, BQT, 512>(Gs[hh], static_cast<const bf16 *>(p.dout) + qpos0 * qrs + (int64_t)h * D,
                                    p.qstride * qrs, nvalid);
             }
             if (tid < BQT * nh) {
@@ -711,7 +713,7 @@ hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
     const int nqblk = (a.Lq + 32 * TB - 1) / (32 * TB);
     const int64_t qgrid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
     if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)kgrid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)kgrid), dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // 32-bit per-lane copy offsets of the d=128 dQ kernel: rows 0..63 of a tile
