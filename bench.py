@@ -130,7 +130,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
     ap.add_argument("--long", action="store_true", help="also time the 32k-token (nL=131072) layers")
-    ap.add_argument("--only", default="", help="comma list of components to run (profiling)")
+    ap.add_argument("--only", default="", help="comma list of components to run (profiling); 'peaks' runs the measured-peak loops alone")
     return ap.parse_args()
 
 
@@ -199,6 +199,9 @@ def main():
     dev = "cuda"
     only = set(x for x in args.only.split(",") if x)
     want = (lambda name: not only or name in only)
+    if only == {"peaks"}:  # profiling: the measured-peak loops alone
+        print(json.dumps({"measured_peaks": measured_peaks(dev)}), flush=True)
+        return
 
     I = synth.INTRA_4K
     I1 = synth.INTRA_4K_N1
