@@ -153,7 +153,15 @@ hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o,
 
 /*
  * Bytes of device workspace hd_sfa_bwd needs for these sizes (0 if the sizes
- * are invalid): one float32 per query row, B*Hq*n*L*4.
+ * are invalid), the larger of the intra and cross layers of the shape (the
+ * window does not change it): one float32 per query row (B*Hq*n*L*4, rounded
+ * up to 256 bytes), then, for bf16 layers whose dK/dV pass would have fewer
+ * than 4096 key waves (B*Hkv*(sub-sequences)*ceil(keys per sub-sequence/32))
+ * and at least 256 queries per sub-sequence, float32 partial dK and dV rows
+ * for nseg segments of the query range: segments of
+ * max(128, ceil(ceil(Lq/want)/32)*32) queries, want = min(8, ceil(4096/waves)),
+ * nseg*B*(sub-sequences)*Hkv*(keys per sub-sequence)*2*d*4 bytes.  For the
+ * n = 1 control at L = 4096, 32/8 heads, d = 128 that is 134 MB.
  */
 size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt);
 
@@ -185,7 +193,10 @@ hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o,
 
 /*
  * Bytes of device workspace hd_sfa_bwd_final needs (0 if the sizes are
- * invalid): one float32 per final-stream query row, B*Hq*L*4.
+ * invalid): one float32 per final-stream query row (B*Hq*L*4, rounded up to
+ * 256 bytes), plus the partial dK/dV rows of the same rule as
+ * hd_sfa_bwd_workspace_bytes with one sub-sequence of L keys (intra) or n*L
+ * keys (cross) and L queries.
  */
 size_t hd_sfa_bwd_final_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt);
 

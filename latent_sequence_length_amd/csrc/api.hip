@@ -2,6 +2,7 @@
 // validation on the host, then dispatch to the HIP kernels on the caller's
 // stream.  No allocation, no synchronisation, no state beyond a thread-local
 // error string.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -237,10 +238,23 @@ hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const in
     return device_status(hd::launch_rope(a, dt == HD_BF16, static_cast<hipStream_t>(stream)), "rope launch");
 }
 
-size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
+// Workspace of a backward call, the larger of the intra and cross layers of
+// this shape (the window does not change it).
+static size_t bwd_ws_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt, bool final_only) {
     if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
     if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;
-    return hd::bwd_workspace_bytes(B, n * L, Hq);
+    size_t need = 0;
+    for (hd_mode mode : {HD_MODE_INTRA, HD_MODE_CROSS}) {
+        hd::BwdArgs a{};
+        a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+        layer_map(a, L, n, mode, 0, final_only);
+        need = std::max(need, hd::bwd_workspace_bytes(a, dt == HD_BF16));
+    }
+    return need;
+}
+
+size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
+    return bwd_ws_bytes(B, L, n, Hq, Hkv, d, dt, false);
 }
 
 static hd_status sfa_bwd_common(const void *q, const void *k, const void *v, const void *o, const void *dout,
@@ -260,15 +274,18 @@ static hd_status sfa_bwd_common(const void *q, const void *k, const void *v, con
     HD_TRY(check_ptr(dv, "dv"));
     HD_TRY(check_ptr(lse, "lse"));
     HD_TRY(check_ptr(workspace, "workspace"));
-    const size_t need = hd::bwd_workspace_bytes(B, final_only ? L : n * L, Hq);
-    if (workspace_bytes < need)
-        return fail(HD_ERR_INVALID, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     hd::BwdArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.drow = static_cast<float *>(workspace);
+    a.dq = dq; a.dk = dk; a.dv = dv;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
     layer_map(a, L, n, mode, window, final_only);
     a.scale = resolve_scale(scale, d);
+    const size_t need = hd::bwd_workspace_bytes(a, dt == HD_BF16);
+    if (workspace_bytes < need)
+        return fail(HD_ERR_INVALID, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    a.drow = static_cast<float *>(workspace);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                       ((size_t)B * Hq * a.qrows * sizeof(float) + 255) / 256 * 256);
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = (dt == HD_BF16) ? hd::launch_sfa_bwd_bf16(a, st) : hd::launch_sfa_bwd_f32(a, st);
     return device_status(e, final_only ? "sfa_bwd_final launch" : "sfa_bwd launch");
@@ -283,9 +300,7 @@ hd_status hd_sfa_bwd(const void *q, const void *k, const void *v, const void *o,
 }
 
 size_t hd_sfa_bwd_final_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt) {
-    if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
-    if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;
-    return hd::bwd_workspace_bytes(B, L, Hq);
+    return bwd_ws_bytes(B, L, n, Hq, Hkv, d, dt, true);
 }
 
 hd_status hd_sfa_bwd_final(const void *q, const void *k, const void *v, const void *o, const void *dout,

@@ -75,12 +75,20 @@ struct BwdArgs {
     const float *lse;  // [B][Hq][qrows], natural log, from the forward
     void *dq, *dk, *dv;
     float *drow;       // workspace [B][Hq][qrows]: D = dO . O per query row
+    float *part;       // workspace after drow: dK/dV partial sums of query segments (or unused)
     int B, nL, Hq, Hkv, d;
     int Lsub, nsub, stride, kbase, weff;
     float scale;
     int Lq, qrows, qsub, qstride, qmul, qadd;
 };
-size_t bwd_workspace_bytes(int B, int qrows, int Hq);
+// Query segments of the dK/dV pass (nseg = 1: one workgroup per key block).
+struct BwdSplit {
+    int nseg, segq;
+};
+BwdSplit bwd_split(const BwdArgs &a);
+// Workspace of one backward call on the mapped layer a: drow, then (bf16
+// path, nseg > 1) the segments' fp32 partial dK/dV rows.
+size_t bwd_workspace_bytes(const BwdArgs &a, bool bf16_path);
 hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st);
 hipError_t launch_sfa_bwd_f32(const BwdArgs &a, hipStream_t st);
 

@@ -19,9 +19,15 @@
 //   1. D_i = dO_i . O_i for every query row (fp32, into the workspace);
 //   2. dK, dV: a workgroup owns 256 keys of one (batch, kv head, sub-sequence)
 //      and walks the query tiles (all heads of the group) that see them,
-//      staging the tiles of up to four heads per barrier;
+//      staging the tiles of up to four heads per barrier.  When the layer has
+//      too few key blocks to fill the chip (the causal triangle then leaves
+//      the first blocks with most of the work), the query range is cut into
+//      segments, each workgroup writes fp32 partial sums for one segment and
+//      a reduction kernel adds the segments in a fixed order;
 //   3. dQ: a wave owns 32 queries of one head and walks the key tiles they see
 //      (the forward's loop, recomputing P from lse), 128 keys per barrier.
+#include <algorithm>
+
 #include "attn_common.h"
 
 namespace hd {
@@ -240,7 +246,7 @@ __device__ __forceinline__ void store_rows(bf16 *out, const f32x16 (&acc)[D / 32
 //   dV^T += dO^T P, dK^T += Q^T dS   [D x 32 k]
 // GQ: the query map is not the identity (final-stream queries).
 template <int D, bool GQ>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p, int nseg, int segq) {
     constexpr int PITCH = 2 * D + 16;
     constexpr int HS = 4;  // heads of the group staged per round
     __shared__ __attribute__((aligned(16))) char Qs[HS][BQT * PITCH];
@@ -252,10 +258,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
     const int g = p.Hq / p.Hkv;
 
-    // workgroup -> (key block, b, kv head, sub); the low key blocks of every
-    // group (they see the most queries) are dispatched first
+    // workgroup -> (key block, query segment, b, kv head, sub); the low key
+    // blocks of every group (they see the most queries) are dispatched first
     const int ngroups = p.B * p.Hkv * p.nsub;
-    const int kblk = (int)(blockIdx.x / ngroups);
+    const int kseg = (int)(blockIdx.x / ngroups);
+    const int kblk = kseg / nseg, seg = kseg % nseg;
     int rest = (int)(blockIdx.x % ngroups);
     const int sub = rest % p.nsub; rest /= p.nsub;
     const int kvh = rest % p.Hkv;
@@ -284,14 +291,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
 
     const float c2 = p.scale * kLog2e;
     const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
-    // queries that see keys [j0, j0 + 128): lim(i) >= j0 and lim(i) - j < weff
-    const int ibeg = first_query(p, j0);
-    const int iend = query_end(p, min(j0 + BKW, p.Lsub) - 1);
+    // queries that see keys [j0, j0 + BKW): lim(i) >= j0 and lim(i) - j < weff,
+    // within this workgroup's segment [seg*segq, qend)
+    const int qend = nseg > 1 ? min(p.Lq, (seg + 1) * segq) : p.Lq;
+    const int ibeg = max(first_query(p, j0), seg * segq);
+    const int iend = min(query_end(p, min(j0 + BKW, p.Lsub) - 1), qend);
+    if (nseg > 1 && ibeg >= iend) return;  // empty segment: the reduction skips it
     for (int h0 = 0; h0 < g; h0 += HS) {
         const int nh = min(HS, g - h0);
         for (int i0 = ibeg; i0 < iend; i0 += BQT) {
             __syncthreads();  // previous tiles consumed
-            const int nvalid = min(BQT, p.Lq - i0);
+            const int nvalid = min(BQT, qend - i0);
             const int64_t qpos0 = q_row(p, b, sub, i0);
             for (int hh = 0; hh < nh; ++hh) {
                 const int h = kvh * g + h0 + hh;
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
             const int lim_first = i0 * qmul + qadd, lim_last = (i0 + BQT - 1) * qmul + qadd;
             const bool active = (lim_last >= jw0) && (p.weff == 0 || lim_first < jw0 + 31 + p.weff) && jw0 < p.Lsub;
             if (!active) continue;
-            const bool need_mask = (lim_first < jw0 + 31) || (i0 + BQT > p.Lq) || (jw0 + 32 > p.Lsub) ||
+            const bool need_mask = (lim_first < jw0 + 31) || (i0 + BQT > qend) || (jw0 + 32 > p.Lsub) ||
                                    (p.weff != 0 && lim_last - jw0 >= p.weff);
             for (int hh = 0; hh < nh; ++hh) {
                 const char *qs = Qs[hh], *gs = Gs[hh];
@@ -334,7 +344,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
                         const int i = i0 + qi, li = i * qmul + qadd;
                         bool vis = true;
                         if (need_mask)
-                            vis = kvalid && i < p.Lq && li >= myk && (p.weff == 0 || li - myk < p.weff);
+                            vis = kvalid && i < qend && li >= myk && (p.weff == 0 || li - myk < p.weff);
                         const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -Ls[hh][qi]));
                         const float pr = vis ? e : 0.f;  // a select, not a branch
                         pop[m2][jj] = (bf16)pr;
@@ -350,11 +360,55 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16_kernel(BwdArgs p) {
             }
         }
     }
-    if (kvalid) {
+    if (kvalid && nseg > 1) {
+        // partial row [seg][b][sub][kvh][j]: dK (unscaled) then dV, fp32
+        float *pr = p.part + (((((int64_t)seg * p.B + b) * p.nsub + sub) * p.Hkv + kvh) * p.Lsub + myk) * (2 * D);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int c = db * 32 + 8 * r4 + 4 * hi;
+                *reinterpret_cast<float4 *>(pr + c) =
+                    float4{dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
+                *reinterpret_cast<float4 *>(pr + D + c) =
+                    float4{dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+            }
+    } else if (kvalid) {
         const int64_t off = kpos * krs + (int64_t)kvh * D;
         store_rows<D>(static_cast<bf16 *>(p.dk) + off, dk, p.scale, hi);
         store_rows<D>(static_cast<bf16 *>(p.dv) + off, dv, 1.f, hi);
     }
+}
+
+// Sum of the segments' partial dK / dV rows in segment order (segments whose
+// query range misses the key's block wrote nothing and are skipped), scaled
+// and rounded to bf16.  One thread per 4 values of a (b, sub, kvh, key) row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdArgs p, int nseg, int segq) {
+    constexpr int C4 = 2 * D / 4;  // float4 chunks per row (dK then dV)
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)p.B * p.nsub * p.Hkv * p.Lsub;
+    if (t >= rows * C4) return;
+    const int c = (int)(t % C4);
+    const int64_t row = t / C4;  // ((b * nsub + sub) * Hkv + kvh) * Lsub + j
+    const int j = (int)(row % p.Lsub);
+    const int kvh = (int)((row / p.Lsub) % p.Hkv);
+    const int sub = (int)((row / p.Lsub / p.Hkv) % p.nsub);
+    const int b = (int)(row / p.Lsub / p.Hkv / p.nsub);
+    const int j0 = j / BKW * BKW;
+    const int ib0 = first_query(p, j0), ie0 = query_end(p, min(j0 + BKW, p.Lsub) - 1);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < nseg; ++s) {
+        const int ib = max(ib0, s * segq), ie = min(ie0, min(p.Lq, (s + 1) * segq));
+        if (ib >= ie) continue;
+        const float4 x = *reinterpret_cast<const float4 *>(p.part + ((int64_t)s * rows + row) * (2 * D) + 4 * c);
+        acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    const bool is_k = 4 * c < D;
+    const float mul = is_k ? p.scale : 1.f;
+    const int dim = is_k ? 4 * c : 4 * c - D;
+    bf16 *out = static_cast<bf16 *>(is_k ? p.dk : p.dv) + (sub_pos(p, b, sub, j) * p.Hkv + kvh) * D + dim;
+    *reinterpret_cast<bf16x4 *>(out) = bf16x4{(bf16)(acc.x * mul), (bf16)(acc.y * mul), (bf16)(acc.z * mul), (bf16)(acc.w * mul)};
 }
 
 // 3. dQ.  Workgroup = 4 waves = HG heads of one GQA group x TB blocks of 32
@@ -713,9 +767,20 @@ hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
     const int nqblk = (a.Lq + 32 * TB - 1) / (32 * TB);
     const int64_t qgrid = (int64_t)nqblk * a.B * a.Hkv * (g / HG) * a.nsub;
     if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)kgrid), dim3(512), 0, st, a);
+    const BwdSplit sp = bwd_split(a);
+    if (kgrid * sp.nseg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)(kgrid * sp.nseg)), dim3(512), 0, st, a,
+                       sp.nseg, sp.segq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (sp.nseg > 1) {
+        const int64_t n4 = (int64_t)a.B * a.nsub * a.Hkv * a.Lsub * (2 * D / 4);
+        if ((n4 + 255) / 256 > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(bwd_dkdv_reduce_kernel<D>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, a,
+                           sp.nseg, sp.segq);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     // 32-bit per-lane copy offsets of the d=128 dQ kernel: rows 0..63 of a tile
     if (D == 128 && (int64_t)64 * a.stride * a.Hkv * D * 2 < ((int64_t)1 << 32)) {
         const int TB2 = DQ_NW / HG;
@@ -749,7 +814,26 @@ hipError_t launch_f32_d(const BwdArgs &a, hipStream_t st) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int B, int qrows, int Hq) { return (size_t)B * Hq * qrows * sizeof(float); }
+BwdSplit bwd_split(const BwdArgs &a) {
+    // key waves (32 keys each) of the dK/dV kernel; below four per SIMD of
+    // the chip the query range is cut into segments of >= 128 queries
+    const int64_t waves = (int64_t)a.B * a.Hkv * a.nsub * ((a.Lsub + 31) / 32);
+    BwdSplit s{1, a.Lq};
+    if (waves >= 4096 || a.Lq < 256) return s;
+    const int want = (int)std::min<int64_t>(8, (4096 + waves - 1) / waves);
+    int segq = (a.Lq + want - 1) / want;
+    segq = std::max(128, (segq + BQT - 1) / BQT * BQT);
+    const int nseg = (a.Lq + segq - 1) / segq;
+    if (nseg > 1) s = BwdSplit{nseg, segq};
+    return s;
+}
+
+size_t bwd_workspace_bytes(const BwdArgs &a, bool bf16_path) {
+    size_t bytes = ((size_t)a.B * a.Hq * a.qrows * sizeof(float) + 255) / 256 * 256;
+    const BwdSplit sp = bf16_path ? bwd_split(a) : BwdSplit{1, a.Lq};
+    if (sp.nseg > 1) bytes += (size_t)sp.nseg * a.B * a.nsub * a.Hkv * a.Lsub * 2 * a.d * sizeof(float);
+    return bytes;
+}
 
 hipError_t launch_sfa_bwd_bf16(const BwdArgs &a, hipStream_t st) {
     hipError_t e = launch_zero_uncovered(a, 2, st);

@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from latent_sequence_length_amd import hd
 
@@ -171,15 +172,52 @@ def test_bwd_final_validation(lib, kw, code):
     assert hd.last_error() != ""
 
 
+def bwd_ws_model(B, L, n, Hq, Hkv, d, final_only):
+    """The documented workspace rule: the per-row D array (rounded up to 256
+    bytes) plus, when the dK/dV pass has fewer than 4096 key waves of 32 keys
+    and at least 256 queries, fp32 partial dK/dV rows of nseg query segments
+    (segments of >= 128 queries, a multiple of 32, at most 8); the larger of
+    the intra and cross layers."""
+    def ceil(a, b):
+        return -(-a // b)
+
+    need = 0
+    for cross in (False, True):
+        if final_only:
+            nsub, Lsub, Lq, qrows = 1, (n * L if cross else L), L, L
+        else:
+            nsub, Lsub = (1, n * L) if cross else (n, L)
+            Lq, qrows = Lsub, n * L
+        total = (B * Hq * qrows * 4 + 255) // 256 * 256
+        waves = B * Hkv * nsub * ((Lsub + 31) // 32)
+        if waves < 4096 and Lq >= 256:
+            want = min(8, ceil(4096, waves))
+            segq = max(128, ceil(ceil(Lq, want), 32) * 32)
+            nseg = ceil(Lq, segq)
+            if nseg > 1:
+                total += nseg * B * nsub * Hkv * Lsub * 2 * d * 4
+        need = max(need, total)
+    return need
+
+
 def test_bwd_workspace_size(lib):
     f = hd.hd_sfa_bwd_workspace_bytes
-    assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4
-    assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4
+    assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4  # 4096 key waves in both layers: D only
+    # n = 1 control: 1024 key waves -> 4 segments of 1024 queries
+    assert f(1, 4096, 1, 32, 8, 128) == 4096 * 32 * 4 + 4 * 8 * 4096 * 2 * 128 * 4
+    # cross layer of 300 positions: 40 key waves -> 3 segments of 128 queries
+    assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4 + 3 * 2 * 2 * 300 * 2 * 64 * 4
     assert f(0, 8, 2, 4, 2, 64) == 0 and f(1, 8, 2, 4, 3, 64) == 0 and f(1, 8, 2, 4, 2, 96) == 0
     ff = hd.hd_sfa_bwd_final_workspace_bytes
-    assert ff(1, 4096, 4, 32, 8, 128) == 4096 * 32 * 4
-    assert ff(2, 100, 3, 8, 2, 64) == 2 * 8 * 100 * 4
+    assert ff(1, 4096, 4, 32, 8, 128) == 4096 * 32 * 4 + 4 * 8 * 4096 * 2 * 128 * 4  # intra: stream 3's keys
+    assert ff(2, 100, 3, 8, 2, 64) == (2 * 8 * 100 * 4 + 255) // 256 * 256
     assert ff(0, 8, 2, 4, 2, 64) == 0 and ff(1, 8, 2, 4, 2, 96) == 0
+    for shape in [(1, 300, 4, 8, 2, 128), (2, 150, 3, 8, 2, 128), (1, 257, 4, 8, 8, 64), (1, 97, 1, 6, 3, 64),
+                  (1, 200, 8, 4, 1, 128), (3, 1, 4, 4, 1, 128), (1, 32768, 4, 16, 4, 128), (4, 1000, 2, 8, 8, 32)]:
+        assert f(*shape) == bwd_ws_model(*shape, False), shape
+        assert ff(*shape) == bwd_ws_model(*shape, True), shape
+    # the float32 path needs the D array only
+    assert f(1, 4096, 1, 32, 8, 128, torch.float32) == 4096 * 32 * 4
 
 
 def test_rope_validation(lib):
