@@ -265,6 +265,8 @@ def main():
 
     if want("bwd_intra_n4"):
         comps["bwd_intra_n4"] = backward(I)
+    if want("bwd_intra_n1"):
+        comps["bwd_intra_n1"] = backward(I1)
     def backward_final(cfg):
         """Backward of the final-stream queries of the layer (KV-mirror
         training): dq of the L final rows, dk/dv of all n*L positions."""
@@ -446,6 +448,12 @@ def main():
                    "n": 4, "seq_len_tokens": 4096, "expanded_len": 16384, "batch": 1,
                    "heads_q": 32, "heads_kv": 8, "head_dim": 128},
         "n4_n1_time_ratio": ratio,
+        # forward + backward of the attention layer (the pages compare training
+        # step times); 4.0 would be the FLOP ratio
+        "n4_n1_train_time_ratio": (round((report["intra_n4"]["ms"] + report["bwd_intra_n4"]["ms"]) /
+                                         (report["intra_n1"]["ms"] + report["bwd_intra_n1"]["ms"]), 3)
+                                   if all(c in report for c in ("intra_n4", "bwd_intra_n4", "intra_n1",
+                                                                "bwd_intra_n1")) else None),
         "decode_GBps": {m: report[m]["GB/s"] for m in ("decode_intra", "decode_cross") if m in report},
         "components": report,
         "step_components": list(step_comps),

@@ -159,9 +159,9 @@ hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o,
  * than 4096 key waves (B*Hkv*(sub-sequences)*ceil(keys per sub-sequence/32))
  * and at least 256 queries per sub-sequence, float32 partial dK and dV rows
  * for nseg segments of the query range: segments of
- * max(128, ceil(ceil(Lq/want)/32)*32) queries, want = min(8, ceil(4096/waves)),
+ * max(128, ceil(ceil(Lq/want)/32)*32) queries, want = min(8, ceil(8192/waves)),
  * nseg*B*(sub-sequences)*Hkv*(keys per sub-sequence)*2*d*4 bytes.  For the
- * n = 1 control at L = 4096, 32/8 heads, d = 128 that is 134 MB.
+ * n = 1 control at L = 4096, 32/8 heads, d = 128 that is 268 MB.
  */
 size_t hd_sfa_bwd_workspace_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt);
 

@@ -816,11 +816,12 @@ hipError_t launch_f32_d(const BwdArgs &a, hipStream_t st) {
 
 BwdSplit bwd_split(const BwdArgs &a) {
     // key waves (32 keys each) of the dK/dV kernel; below four per SIMD of
-    // the chip the query range is cut into segments of >= 128 queries
+    // the chip the query range is cut into segments of >= 128 queries, about
+    // 8192 / waves of them (at most 8)
     const int64_t waves = (int64_t)a.B * a.Hkv * a.nsub * ((a.Lsub + 31) / 32);
     BwdSplit s{1, a.Lq};
     if (waves >= 4096 || a.Lq < 256) return s;
-    const int want = (int)std::min<int64_t>(8, (4096 + waves - 1) / waves);
+    const int want = (int)std::min<int64_t>(8, (8192 + waves - 1) / waves);
     int segq = (a.Lq + want - 1) / want;
     segq = std::max(128, (segq + BQT - 1) / BQT * BQT);
     const int nseg = (a.Lq + segq - 1) / segq;

@@ -176,8 +176,8 @@ def bwd_ws_model(B, L, n, Hq, Hkv, d, final_only):
     """The documented workspace rule: the per-row D array (rounded up to 256
     bytes) plus, when the dK/dV pass has fewer than 4096 key waves of 32 keys
     and at least 256 queries, fp32 partial dK/dV rows of nseg query segments
-    (segments of >= 128 queries, a multiple of 32, at most 8); the larger of
-    the intra and cross layers."""
+    (about 8192 / waves segments, at most 8, of >= 128 queries, a multiple of
+    32); the larger of the intra and cross layers."""
     def ceil(a, b):
         return -(-a // b)
 
@@ -191,7 +191,7 @@ def bwd_ws_model(B, L, n, Hq, Hkv, d, final_only):
         total = (B * Hq * qrows * 4 + 255) // 256 * 256
         waves = B * Hkv * nsub * ((Lsub + 31) // 32)
         if waves < 4096 and Lq >= 256:
-            want = min(8, ceil(4096, waves))
+            want = min(8, ceil(8192, waves))
             segq = max(128, ceil(ceil(Lq, want), 32) * 32)
             nseg = ceil(Lq, segq)
             if nseg > 1:
@@ -203,13 +203,13 @@ def bwd_ws_model(B, L, n, Hq, Hkv, d, final_only):
 def test_bwd_workspace_size(lib):
     f = hd.hd_sfa_bwd_workspace_bytes
     assert f(1, 4096, 4, 32, 8, 128) == 4096 * 4 * 32 * 4  # 4096 key waves in both layers: D only
-    # n = 1 control: 1024 key waves -> 4 segments of 1024 queries
-    assert f(1, 4096, 1, 32, 8, 128) == 4096 * 32 * 4 + 4 * 8 * 4096 * 2 * 128 * 4
+    # n = 1 control: 1024 key waves -> 8 segments of 512 queries
+    assert f(1, 4096, 1, 32, 8, 128) == 4096 * 32 * 4 + 8 * 8 * 4096 * 2 * 128 * 4
     # cross layer of 300 positions: 40 key waves -> 3 segments of 128 queries
     assert f(2, 100, 3, 8, 2, 64) == 2 * 8 * 300 * 4 + 3 * 2 * 2 * 300 * 2 * 64 * 4
     assert f(0, 8, 2, 4, 2, 64) == 0 and f(1, 8, 2, 4, 3, 64) == 0 and f(1, 8, 2, 4, 2, 96) == 0
     ff = hd.hd_sfa_bwd_final_workspace_bytes
-    assert ff(1, 4096, 4, 32, 8, 128) == 4096 * 32 * 4 + 4 * 8 * 4096 * 2 * 128 * 4  # intra: stream 3's keys
+    assert ff(1, 4096, 4, 32, 8, 128) == 4096 * 32 * 4 + 8 * 8 * 4096 * 2 * 128 * 4  # intra: stream 3's keys
     assert ff(2, 100, 3, 8, 2, 64) == (2 * 8 * 100 * 4 + 255) // 256 * 256
     assert ff(0, 8, 2, 4, 2, 64) == 0 and ff(1, 8, 2, 4, 2, 96) == 0
     for shape in [(1, 300, 4, 8, 2, 128), (2, 150, 3, 8, 2, 128), (1, 257, 4, 8, 8, 64), (1, 97, 1, 6, 3, 64),
