@@ -32,6 +32,13 @@ __device__ __forceinline__ void lds_dma16_s(const void *base, unsigned voff, uns
                  : "memory", "m0");
 }
 
+// Direct-to-LDS 4-byte load: lane l's dword from base + voff lands at LDS
+// byte address lds_base + 4*l (same conventions as lds_dma16_s).
+__device__ __forceinline__ void lds_dma4_s(const void *base, unsigned voff, unsigned lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds_base), "v"(voff), "s"(base)
+                 : "memory", "m0");
+}
+
 __device__ __forceinline__ unsigned lds_addr(const char *p) {
     return (unsigned)(size_t)((__attribute__((address_space(3))) const char *)p);
 }

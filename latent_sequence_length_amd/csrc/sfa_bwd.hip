@@ -719,6 +719,214 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
     if (qvalid) store_rows<D>(static_cast<bf16 *>(p.dq) + qrow * qrs + (int64_t)h * D, dq, p.scale, hi);
 }
 
+// dK, dV for d = 128: the workgroup of the generic kernel above (8 waves x 32
+// keys, K^T and V^T held as B operands in registers), with each round's
+// query tiles (Q and dO rows of up to four heads, 64 KB) and their lse / D
+// values copied direct to LDS and double-buffered, so the next round's copy
+// is in flight while this round is computed.  Tiles are stored unpadded with
+// row r's 16-byte chunks XOR-swizzled by swzv(r): conflict-free for the row
+// reads of S = Q K^T and dP = dO V^T (32 rows, one chunk) and for the
+// transposed reads of dV^T += dO^T P and dK^T += Q^T dS.
+constexpr int DKV_NW = 8;  // waves (32 keys each) per workgroup
+constexpr int DKV_HS = 4;  // heads of the group per round
+
+template <bool GQ>
+__global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p, int nseg, int segq) {
+    constexpr int D = 128, QT = 32;
+    constexpr int QTILE = QT * D * 2;          // 8 KB: 32 rows of one head
+    constexpr int RB = 2 * DKV_HS * QTILE;     // Q tiles | dO tiles of a round
+    __shared__ __attribute__((aligned(4096))) char tb0[RB];
+    __shared__ __attribute__((aligned(4096))) char tb1[RB];
+    __shared__ __attribute__((aligned(256))) float sb0[2][DKV_HS][QT];  // lse | D of the rows
+    __shared__ __attribute__((aligned(256))) float sb1[2][DKV_HS][QT];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
+    const int g = p.Hq / p.Hkv;
+
+    const int ngroups = p.B * p.Hkv * p.nsub;
+    const int kseg = (int)(blockIdx.x / ngroups);
+    const int kblk = kseg / nseg, seg = kseg % nseg;
+    int rest = (int)(blockIdx.x % ngroups);
+    const int sub = rest % p.nsub; rest /= p.nsub;
+    const int kvh = rest % p.Hkv;
+    const int b = rest / p.Hkv;
+    const int j0 = kblk * BKW;
+    const int jw0 = j0 + 32 * wave;
+    const int myk = jw0 + l32;
+    const bool kvalid = myk < p.Lsub;
+
+    const int qend = nseg > 1 ? min(p.Lq, (seg + 1) * segq) : p.Lq;
+    const int ibeg = max(first_query(p, j0), seg * segq);
+    const int iend = min(query_end(p, min(j0 + BKW, p.Lsub) - 1), qend);
+    if (nseg > 1 && ibeg >= iend) return;  // empty segment: the reduction skips it
+
+    const int64_t qrs = (int64_t)p.Hq * D, krs = (int64_t)p.Hkv * D;
+    const int64_t kpos = sub_pos(p, b, sub, kvalid ? myk : 0);
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const bf16 *kr = static_cast<const bf16 *>(p.k) + kpos * krs + (int64_t)kvh * D + 8 * hi;
+        const bf16 *vr = static_cast<const bf16 *>(p.v) + kpos * krs + (int64_t)kvh * D + 8 * hi;
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+            kf[ks] = kvalid ? *reinterpret_cast<const bf16x8 *>(kr + 16 * ks) : bf16x8{};
+            vf[ks] = kvalid ? *reinterpret_cast<const bf16x8 *>(vr + 16 * ks) : bf16x8{};
+        }
+    }
+    f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dk[db] = dv[db] = f32x16{};
+
+    const float c2 = p.scale * kLog2e;
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    const int ntq = iend > ibeg ? (iend - ibeg + QT - 1) / QT : 0;
+    const int nrounds = ntq * ((g + DKV_HS - 1) / DKV_HS);
+
+    // copy-in: wave w moves the 32 rows of tensor w / 4 (Q, dO) of head w % 4,
+    // 4 rows per instruction; lane l fills physical chunk l % 16 of row
+    // 4i + l/16 with logical chunk (l % 16) ^ swzv(row), and swzv(4i + l/16) =
+    // 4*(l/16) + i%4, so four per-lane offsets serve all eight instructions
+    const int ct = wave / DKV_HS, chh = wave % DKV_HS;
+    const int rs = p.qstride * (int)qrs;  // elements between consecutive query rows
+    unsigned voff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        voff[m] = (unsigned)((lane >> 4) * rs + (((lane & 15) ^ (4 * (lane >> 4) + m)) * 8)) * 2u;
+    auto issue = [&](int k, char *tb, float (*sb)[DKV_HS][QT]) {
+        const int h0 = (k / ntq) * DKV_HS, i0 = ibeg + (k % ntq) * QT;
+        const int nh = min(DKV_HS, g - h0);
+        const int nvalid = min(QT, qend - i0);
+        const int64_t qpos0 = q_row(p, b, sub, i0);
+        if (chh < nh) {
+            const bf16 *src = static_cast<const bf16 *>(ct ? p.dout : p.q) + qpos0 * qrs + (int64_t)(kvh * g + h0 + chh) * D;
+            char *dst = tb + (ct * DKV_HS + chh) * QTILE;
+            if (nvalid == QT) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    lds_dma16_s(src + (int64_t)i * 4 * rs, voff[i & 3], lds_addr(dst + i * 1024));
+            } else {  // tail: rows past the segment re-read its last row (masked later)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = 4 * i + (lane >> 4);
+                    const unsigned vo = (unsigned)(min(r, nvalid - 1) * rs + (((lane & 15) ^ swzv(r)) * 8)) * 2u;
+                    lds_dma16_s(src, vo, lds_addr(dst + i * 1024));
+                }
+            }
+        }
+        if (wave == 0) {  // lse and D of the round's rows: 2 heads x 32 rows per instruction
+#pragma unroll
+            for (int j = 0; j < DKV_HS / 2; ++j) {
+                const int hh = min(2 * j + (lane >> 5), nh - 1);
+                const int64_t qr = qpos0 + (int64_t)min(l32, nvalid - 1) * p.qstride;
+                const unsigned so = (unsigned)row_stat(p, b, kvh * g + h0 + hh, qr) * 4u;
+                lds_dma4_s(p.lse, so, lds_addr(reinterpret_cast<char *>(&sb[0][2 * j][0])));
+                lds_dma4_s(p.drow, so, lds_addr(reinterpret_cast<char *>(&sb[1][2 * j][0])));
+            }
+        }
+    };
+
+    // LDS read addresses: the lane's offset within a tile for k-step 0 (row
+    // reads) and for (m2, db, jh) = 0 (transposed reads); the others follow by
+    // XOR with a constant (the swizzle only permutes bits 4..7 of a row, and
+    // tiles are 4 KB aligned), so each read costs one v_xor, not a register
+    const int rsw = swzv(l32);
+    const unsigned aoff = (unsigned)(l32 * 256 + ((hi ^ rsw) << 4));  // ks -> aoff ^ (ks << 5)
+    unsigned toff;  // (m2, db, jh) -> (toff ^ (64*db + 2080*jh)) + 4096*m2
+    {
+        const int row = 4 * hi + (l16 >> 2), dim = 16 * g2 + 4 * (l16 & 3);
+        toff = (unsigned)(row * 256 + (((dim >> 3) ^ swzv(row)) << 4) + ((dim >> 2) & 1) * 8);
+    }
+    auto round = [&](int k, const char *tb, const float (*sb)[DKV_HS][QT]) {
+        const int h0 = (k / ntq) * DKV_HS, i0 = ibeg + (k % ntq) * QT;
+        const int nh = min(DKV_HS, g - h0);
+        const int lim_first = i0 * qmul + qadd, lim_last = (i0 + QT - 1) * qmul + qadd;
+        const bool active = (lim_last >= jw0) && (p.weff == 0 || lim_first < jw0 + 31 + p.weff) && jw0 < p.Lsub;
+        if (!active) return;
+        const bool need_mask = (lim_first < jw0 + 31) || (i0 + QT > qend) || (jw0 + 32 > p.Lsub) ||
+                               (p.weff != 0 && lim_last - jw0 >= p.weff);
+        for (int hh = 0; hh < nh; ++hh) {
+            unsigned qa = lds_addr(tb + hh * QTILE) + aoff, qt = lds_addr(tb + hh * QTILE) + toff;
+            asm volatile("" : "+v"(qa), "+v"(qt));  // keep the derived addresses per use
+            constexpr unsigned GOFF = DKV_HS * QTILE;  // dO tile of the same head
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                const unsigned a = qa ^ (unsigned)(ks << 5);
+                s = mfma32(*reinterpret_cast<__attribute__((address_space(3))) const bf16x8 *>((size_t)a), kf[ks], s);
+                dp = mfma32(*reinterpret_cast<__attribute__((address_space(3))) const bf16x8 *>((size_t)(a + GOFF)),
+                            vf[ks], dp);
+            }
+            // register r = 8*m2 + jj holds query 16*m2 + 8*(jj/4) + 4*hi + jj%4
+            bf16x8 pop[2], dsop[2];
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int r = 8 * m2 + jj;
+                    const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
+                    const int i = i0 + qi, li = i * qmul + qadd;
+                    bool vis = true;
+                    if (need_mask) vis = kvalid && i < qend && li >= myk && (p.weff == 0 || li - myk < p.weff);
+                    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sb[0][hh][qi] * kLog2e));
+                    const float pr = vis ? e : 0.f;  // a select, not a branch
+                    pop[m2][jj] = (bf16)pr;
+                    dsop[m2][jj] = (bf16)(pr * (dp[r] - sb[1][hh][qi]));
+                }
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    s16x4 hg[2], hq[2];
+#pragma unroll
+                    for (int jh = 0; jh < 2; ++jh) {
+                        const unsigned a = (qt ^ (unsigned)(64 * db + 2080 * jh)) + 4096u * m2;
+                        hq[jh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            reinterpret_cast<__attribute__((address_space(3))) s16x4 *>((size_t)a));
+                        hg[jh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            reinterpret_cast<__attribute__((address_space(3))) s16x4 *>((size_t)(a + GOFF)));
+                    }
+                    const s16x8 bg = __builtin_shufflevector(hg[0], hg[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    const s16x8 bq = __builtin_shufflevector(hq[0], hq[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    dv[db] = mfma32(__builtin_bit_cast(bf16x8, bg), pop[m2], dv[db]);
+                    dk[db] = mfma32(__builtin_bit_cast(bf16x8, bq), dsop[m2], dk[db]);
+                }
+        }
+    };
+
+    if (nrounds > 0) issue(0, tb0, sb0);
+    for (int k = 0; k < nrounds; k += 2) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of round k have landed
+        __syncthreads();                // ... and every wave's; round k-1 fully consumed
+        if (k + 1 < nrounds) issue(k + 1, tb1, sb1);
+        round(k, tb0, sb0);
+        if (k + 1 < nrounds) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (k + 2 < nrounds) issue(k + 2, tb0, sb0);
+            round(k + 1, tb1, sb1);
+        }
+    }
+
+    if (kvalid && nseg > 1) {
+        float *pr = p.part + (((((int64_t)seg * p.B + b) * p.nsub + sub) * p.Hkv + kvh) * p.Lsub + myk) * (2 * D);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int c = db * 32 + 8 * r4 + 4 * hi;
+                *reinterpret_cast<float4 *>(pr + c) =
+                    float4{dk[db][4 * r4], dk[db][4 * r4 + 1], dk[db][4 * r4 + 2], dk[db][4 * r4 + 3]};
+                *reinterpret_cast<float4 *>(pr + D + c) =
+                    float4{dv[db][4 * r4], dv[db][4 * r4 + 1], dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]};
+            }
+    } else if (kvalid) {
+        const int64_t off = kpos * krs + (int64_t)kvh * D;
+        store_rows<D>(static_cast<bf16 *>(p.dk) + off, dk, p.scale, hi);
+        store_rows<D>(static_cast<bf16 *>(p.dv) + off, dv, 1.f, hi);
+    }
+}
+
 // dK and dV rows that no key sub-sequence covers (the other streams of a
 // final-stream intra layer: position t is covered iff (t - kbase) mod stride
 // < nsub) receive no gradient: write zeros, 16 bytes per thread.
@@ -769,8 +977,16 @@ hipError_t launch_bf16_d(const BwdArgs &a, hipStream_t st) {
     if (kgrid > 0x7fffffff || qgrid > 0x7fffffff) return hipErrorInvalidConfiguration;
     const BwdSplit sp = bwd_split(a);
     if (kgrid * sp.nseg > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)(kgrid * sp.nseg)), dim3(512), 0, st, a,
-                       sp.nseg, sp.segq);
+    // the d=128 kernel's per-lane copy offsets are 32-bit: 31 query rows +
+    // 256 B, and the lse / D index of any row, in bytes
+    if (D == 128 && (int64_t)31 * a.qstride * a.Hq * D * 2 + 256 < ((int64_t)1 << 32) &&
+        (int64_t)a.B * a.Hq * a.qrows * 4 < ((int64_t)1 << 32)) {
+        hipLaunchKernelGGL((bwd_dkdv_d128_kernel<GQ>), dim3((unsigned)(kgrid * sp.nseg)), dim3(64 * DKV_NW), 0, st,
+                           a, sp.nseg, sp.segq);
+    } else {
+        hipLaunchKernelGGL((bwd_dkdv_bf16_kernel<D, GQ>), dim3((unsigned)(kgrid * sp.nseg)), dim3(512), 0, st, a,
+                           sp.nseg, sp.segq);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (sp.nseg > 1) {
