@@ -676,17 +676,23 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
                 }
         }
         // register r of block kb holds key t0 + 32*kb + 8*(r/4) + 4*hi + r%4
+        bf16x8 dsall[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-                bf16x8 dsop;
+            for (int m2 = 0; m2 < 2; ++m2)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int r = 8 * m2 + j;
                     const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], c2, -lse2));
-                    dsop[j] = (bf16)(pr * (dp[kb][r] - Dq));
+                    dsall[kb * 2 + m2][j] = (bf16)(pr * (dp[kb][r] - Dq));
                 }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int m2 = 0; m2 < 2; ++m2) {
+                const bf16x8 dsop = dsall[kb * 2 + m2];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
                     s16x4 half[2];
@@ -701,6 +707,17 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
                     dq[db] = mfma32(__builtin_bit_cast(bf16x8, both), dsop, dq[db]);
                 }
             }
+        // the 32 transposed K reads run eight ahead of the 16 dQ MFMAs, two
+        // per MFMA after that (sched_group_barrier masks: 0x100 LDS reads,
+        // 0x008 MFMA)
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
     };
 
     for (int it = 0; it < ntiles; it += 2) {
@@ -891,6 +908,16 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
                     dv[db] = mfma32(__builtin_bit_cast(bf16x8, bg), pop[m2], dv[db]);
                     dk[db] = mfma32(__builtin_bit_cast(bf16x8, bq), dsop[m2], dk[db]);
                 }
+            // the 32 transposed reads run eight ahead of the 16 dV/dK MFMAs,
+            // two per MFMA after that
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < 12; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
