@@ -93,6 +93,12 @@ BWD_SHAPES = [
     ((1, 160, 4, 8, 2, 128), CROSS, 10),    # local cross-stream window
     ((3, 1, 4, 4, 1, 128), INTRA, 0),       # one token
     ((1, 1, 1, 2, 1, 64), CROSS, 0),        # one position
+    ((1, 100, 2, 4, 4, 128), CROSS, 0),     # d=128 MHA: one head per staged round
+    ((1, 90, 3, 4, 2, 128), INTRA, 0),      # d=128, g=2
+    ((1, 70, 2, 6, 2, 128), CROSS, 5),      # d=128, g=3, window
+    ((1, 80, 2, 12, 2, 128), INTRA, 0),     # d=128, g=6: head rounds of 4 then 2
+    ((1, 600, 1, 4, 1, 128), CROSS, 0),     # 5 query segments of the dK/dV pass + reduction
+    ((2, 520, 1, 8, 2, 128), INTRA, 100),   # segments with a window: empty ones skipped
 ]
 
 

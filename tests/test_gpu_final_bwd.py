@@ -90,6 +90,8 @@ FINAL_BWD_SHAPES = [
     ((1, 200, 8, 4, 1, 128), CROSS, 3),     # n=8
     ((3, 1, 4, 4, 1, 128), CROSS, 0),       # one token
     ((1, 1, 1, 2, 1, 64), INTRA, 0),        # one position
+    ((1, 300, 4, 4, 2, 128), INTRA, 0),     # g=2; 3 query segments of the dK/dV pass
+    ((1, 90, 3, 6, 2, 128), CROSS, 4),      # g=3, window
 ]
 
 
