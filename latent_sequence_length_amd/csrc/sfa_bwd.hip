@@ -867,6 +867,7 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
             asm volatile("" : "+v"(qa), "+v"(qt));  // keep the derived addresses per use
             constexpr unsigned GOFF = DKV_HS * QTILE;  // dO tile of the same head
             f32x16 s = f32x16{}, dp = f32x16{};
+            __builtin_amdgcn_s_setprio(1);  // MFMA phases win issue arbitration over the other wave's VALU
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 const unsigned a = qa ^ (unsigned)(ks << 5);
@@ -874,6 +875,7 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
                 dp = mfma32(*reinterpret_cast<__attribute__((address_space(3))) const bf16x8 *>((size_t)(a + GOFF)),
                             vf[ks], dp);
             }
+            __builtin_amdgcn_s_setprio(0);
             // register r = 8*m2 + jj holds query 16*m2 + 8*(jj/4) + 4*hi + jj%4
             bf16x8 pop[2], dsop[2];
 #pragma unroll
@@ -910,6 +912,7 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
                 }
             // the 32 transposed reads run eight ahead of the 16 dV/dK MFMAs,
             // two per MFMA after that
+            __builtin_amdgcn_s_setprio(1);
             __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
             for (int i = 0; i < 12; ++i) {
@@ -918,6 +921,7 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
