@@ -18,14 +18,17 @@
 // Three launches, no atomics, every output element written once:
 //   1. D_i = dO_i . O_i for every query row (fp32, into the workspace);
 //   2. dK, dV: a workgroup owns 256 keys of one (batch, kv head, sub-sequence)
-//      and walks the query tiles (all heads of the group) that see them,
-//      staging the tiles of up to four heads per barrier.  When the layer has
-//      too few key blocks to fill the chip (the causal triangle then leaves
-//      the first blocks with most of the work), the query range is cut into
-//      segments, each workgroup writes fp32 partial sums for one segment and
-//      a reduction kernel adds the segments in a fixed order;
+//      and walks the query tiles (all heads of the group) that see them, the
+//      tiles of up to four heads per round (d = 128: copied direct to LDS and
+//      double-buffered; d = 32/64: staged through registers).  When the layer
+//      has too few key blocks to fill the chip (the causal triangle then
+//      leaves the first blocks with most of the work), the query range is cut
+//      into segments, each workgroup writes fp32 partial sums for one segment
+//      and a reduction kernel adds the segments in a fixed order;
 //   3. dQ: a wave owns 32 queries of one head and walks the key tiles they see
-//      (the forward's loop, recomputing P from lse), 128 keys per barrier.
+//      (the forward's loop, recomputing P from lse); d = 128 shares 64-key
+//      tiles copied direct to LDS among 8 waves, d = 32/64 stages 128 keys per
+//      barrier through registers.
 #include <algorithm>
 
 #include "attn_common.h"
