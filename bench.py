@@ -10,25 +10,30 @@ are already resident in HBM:
                  intra and cross (one new token, 4 stream queries each)
 After the timed steps, the extension rows are timed in a loop of their own
 (reported under "components", outside ms_per_step):
+  gather         the same tables at prefill size: B=1, L=4096, n=4 -> 16384 rows
+                 (0.47 GB moved; 64 rotating id sets so rows come from HBM)
+  long context   n=4, L=32768 (nL=131072), 16 q / 4 kv heads: intra-stream with
+                 a 4096-token window, local cross-stream with a 4096-token window,
+                 and a full cross-stream layer
   final-stream   the final stream's queries of the headline shapes (intra and
                  cross) and the backward of the cross one; decode of the final
                  stream's query (intra and cross)
   rotary embed   q and k of the headline layer at the expanded positions, and
                  the prefill with the rotation of q fused in
   backward       dQ, dK, dV of the headline intra-stream layer (given o, lse, dO)
-With --long, also the 32k-token layers (n=4, nL=131072, 16 q / 4 kv heads):
-intra-stream with a 4096-token window, local cross-stream with a 4096-token
-window, and a full cross-stream layer.
 Each call is timed with HIP events on the stream it is launched on.  The
 headline value is useful TFLOP/s of the intra-stream prefill (4*d*Hq FLOPs per
-visible query/key pair).  Prints one JSON line.
+visible query/key pair).  Beside the GPU rows: the CPU oracle timed on a
+bounded sample of each step row (and of the gather and long-context rows) on
+this host's cores, and the machine's measured matrix-core and HBM-read rates.
+Prints one JSON line.
 """
 import argparse
 import ctypes
 import hashlib
 import json
-import math
 import os
+import subprocess
 import sys
 import time
 
@@ -38,19 +43,38 @@ import torch
 from latent_sequence_length_amd import hd, synth
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
-PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
+PROBE_SRC = os.path.join(ROOT, "bench_peaks.hip")
+PROBE_LIB = os.path.join(ROOT, "bench_peaks.so")
+
+
+def build_probe(verbose=False):
+    """Compile the measured-peak probes (bench_peaks.hip) for gfx950."""
+    arch = os.environ.get("HD_OFFLOAD_ARCH", "gfx950")
+    cmd = ["hipcc", f"--offload-arch={arch}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC}:\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
+def _tri(T, w):
+    """Sum over q in [0, T) of min(q + 1, w) (w = 0: no window)."""
+    if w <= 0 or w >= T:
+        return T * (T + 1) // 2
+    return w * (w + 1) // 2 + (T - w) * w
 
 
 def useful_flops(B, L, n, Hq, d, mode, window=0):
     """4*d*Hq*(number of visible (query, key) pairs): QK^T and PV, 2 flops per
     multiply-add.  Intra: per stream, tokens j <= i within the window; cross:
     positions t_k <= t_q within n*window positions."""
-    def tri(T, w):  # sum over q in [0, T) of min(q + 1, w) (w = 0: no window)
-        if w <= 0 or w >= T:
-            return T * (T + 1) // 2
-        return w * (w + 1) // 2 + (T - w) * w
-    pairs = n * tri(L, window) if mode == 0 else tri(n * L, n * window)
+    pairs = n * _tri(L, window) if mode == 0 else _tri(n * L, n * window)
     return 4.0 * d * Hq * B * pairs
 
 
@@ -58,27 +82,35 @@ def useful_flops_final(B, L, n, Hq, d, mode, window=0):
     """Final-stream queries of a KV-mirror layer: query i sees tokens
     j <= i (within the window) of stream n-1 only (intra) or of all n
     streams (cross)."""
-    def tri(T, w):
-        if w <= 0 or w >= T:
-            return T * (T + 1) // 2
-        return w * (w + 1) // 2 + (T - w) * w
-    pairs = tri(L, window) * (n if mode == 1 else 1)
+    pairs = _tri(L, window) * (n if mode == 1 else 1)
     return 4.0 * d * Hq * B * pairs
+
+
+def row_visible_keys(t, n, L, mode, window):
+    """Visible keys of query position(s) t of a prefill layer (numpy)."""
+    if mode == 0:
+        i = t // n + 1
+        return np.minimum(i, window) if window else i
+    return np.minimum(t + 1, n * window) if window else t + 1
 
 
 def measured_peaks(dev):
     """The machine's sustained rates, reported beside the published peaks:
-    an MFMA-only loop (libhd_probe.so, 8 independent bf16 32x32x16 chains
-    per wave, 4 waves per SIMD) and a 1 GiB device copy (read + write)."""
+    an MFMA-only loop (8 independent bf16 32x32x16 chains per wave, 4 waves
+    per SIMD), a read-only stream over 8 GiB (16-byte non-temporal loads; the
+    HBM ceiling of a read-dominated kernel such as decode) and, for context,
+    a 1 GiB device copy (read + write, torch)."""
     out = {}
-    path = os.path.join(ROOT, "latent_sequence_length_amd", "libhd_probe.so")
-    if os.path.exists(path):
-        lib = ctypes.CDLL(path)
+    if os.path.exists(PROBE_LIB):
+        lib = ctypes.CDLL(PROBE_LIB)
         lib.hd_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.hd_probe_mfma_bf16.restype = ctypes.c_double
+        lib.hd_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        lib.hd_probe_hbm_read.restype = ctypes.c_double
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         blocks, iters = 4096, 2048
         sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         lib.hd_probe_mfma_bf16(blocks, iters, ctypes.c_void_p(sink.data_ptr()), st)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
@@ -87,6 +119,20 @@ def measured_peaks(dev):
         torch.cuda.synchronize()
         if fl > 0:
             out["mfma_bf16_TFLOPs"] = round(fl / s.elapsed_time(e) / 1e9, 1)
+        del sink
+        nbytes = 8 << 30
+        buf = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device=dev)
+        rblocks = 256 * 8
+        rsink = torch.empty(rblocks * 256, dtype=torch.int32, device=dev)
+        args = (ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks, ctypes.c_void_p(rsink.data_ptr()), st)
+        lib.hd_probe_hbm_read(*args)
+        s.record()
+        by = sum(lib.hd_probe_hbm_read(*args) for _ in range(5))
+        e.record()
+        torch.cuda.synchronize()
+        if by > 0:
+            out["hbm_read_GBps"] = round(by / s.elapsed_time(e) / 1e6, 1)
+        del buf, rsink
     src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
     dst = torch.empty_like(src)
     dst.copy_(src)
@@ -96,7 +142,7 @@ def measured_peaks(dev):
         dst.copy_(src)
     e.record()
     torch.cuda.synchronize()
-    out["copy_GBps"] = round(5 * 2 * src.numel() * 2 / s.elapsed_time(e) / 1e6, 1)
+    out["copy_rw_GBps"] = round(5 * 2 * src.numel() * 2 / s.elapsed_time(e) / 1e6, 1)
     return out
 
 
@@ -128,9 +174,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline leg")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-oracle sample budget")
-    ap.add_argument("--long", action="store_true", help="also time the 32k-token (nL=131072) layers")
-    ap.add_argument("--only", default="", help="comma list of components to run (profiling); 'peaks' runs the measured-peak loops alone")
+    ap.add_argument("--cpu-seconds", type=float, default=24.0, help="CPU-oracle sample budget over all rows")
+    ap.add_argument("--no-extra", action="store_true", help="time the step rows only")
+    ap.add_argument("--only", default="", help="comma list of components to run (profiling); 'peaks' runs the "
+                                               "measured-peak loops alone")
     return ap.parse_args()
 
 
@@ -156,37 +203,91 @@ class Timer:
         self.pending = []
 
 
-def cpu_baseline(budget_s):
-    """Time the oracle on a bounded random sample of the headline workload."""
+# ---------------------------------------------------------------------------
+# CPU-oracle baselines: the oracle as it stands, on a bounded sample of each
+# row's workload, on the same inputs as the GPU (host copies), extrapolated to
+# the whole row by its share of the work.
+# ---------------------------------------------------------------------------
+
+def _cores():
+    return int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
+
+
+def _time_prefill_rows(q, k, v, cfg, budget_s, seed):
+    """Random query rows of a prefill layer through the oracle until the
+    budget is spent; returns (useful flops done, seconds, rows)."""
     import oracle
 
-    c = synth.INTRA_4K
-    q, k, v = synth.qkv(c.B, c.L, c.n, c.Hq, c.Hkv, c.d, c.dtype, "cpu")
-    nL = c.n * c.L
-    rng = np.random.default_rng(123)
-    oracle.sfa_rows(q, k, v, c.n, c.mode, c.window, rows=np.array([0], dtype=np.int64))  # load + warm
-    flops = 0.0
-    rows_done = 0
+    nL = cfg.n * cfg.L
+    total = cfg.B * nL * cfg.Hq
+    rng = np.random.default_rng(seed)
+    oracle.sfa_rows(q, k, v, cfg.n, cfg.mode, cfg.window, rows=np.array([0], dtype=np.int64))  # load + warm
+    flops, rows_done, batch = 0.0, 0, 32
     t0 = time.perf_counter()
-    batch = 256
-    while time.perf_counter() - t0 < budget_s:
-        rows = rng.integers(0, c.B * nL * c.Hq, batch).astype(np.int64)
-        oracle.sfa_rows(q, k, v, c.n, c.mode, c.window, rows=rows)
-        t = (rows // c.Hq) % nL
-        visible = t // c.n + 1  # intra, no window: tokens 0..i of the query's stream
-        flops += float(4 * c.d * visible.sum())
+    while rows_done < total:
+        rows = rng.integers(0, total, batch).astype(np.int64)
+        oracle.sfa_rows(q, k, v, cfg.n, cfg.mode, cfg.window, rows=rows)
+        t = (rows // cfg.Hq) % nL
+        flops += float(4 * cfg.d * row_visible_keys(t, cfg.n, cfg.L, cfg.mode, cfg.window).sum())
         rows_done += batch
-        batch = min(batch * 2, 8192)
+        spent = time.perf_counter() - t0
+        if spent >= budget_s * 0.95:
+            break
+        # size the next batch to the time that is left, from the rate so far
+        batch = int(min(8192, max(16, (budget_s - spent) * rows_done / spent)))
+    return flops, time.perf_counter() - t0, rows_done
+
+
+def cpu_prefill(cfg, budget_s, seed, gpu_inputs=None):
+    """CPU-oracle rate on one prefill layer (inputs: host copies of the GPU's)."""
+    if gpu_inputs is not None:
+        q, k, v = (t.cpu() for t in gpu_inputs)
+    else:
+        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, "cuda")
+        q, k, v = q.cpu(), k.cpu(), v.cpu()
+    fl, dt, rows = _time_prefill_rows(q, k, v, cfg, budget_s, seed)
+    total_fl = useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+    rate = fl / dt
+    nrows = cfg.B * cfg.n * cfg.L * cfg.Hq
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "ms_extrapolated": round(total_fl / rate * 1e3, 1),
+            "extrapolated": True,
+            "sample": f"{rows} random query rows of {nrows} ({rows / nrows:.2%}), {dt:.1f} s"}
+
+
+def cpu_decode(dq, dkn, dvn, dkc, dvc, ctx, mode, nseq, by_total):
+    """CPU-oracle rate on the decode step, on the first nseq of its sequences
+    (each sequence is an independent step); GB/s counts the same bytes per
+    sequence as the GPU row."""
+    import oracle
+
+    B = dq.shape[0]
+    q, kn, vn = dq[:nseq].cpu(), dkn[:nseq].cpu(), dvn[:nseq].cpu()
+    kc, vc = dkc[:nseq, :ctx + 1].cpu().contiguous(), dvc[:nseq, :ctx + 1].cpu().contiguous()
+    lens = [ctx] * nseq
+    t0 = time.perf_counter()
+    oracle.sfa_decode(q, kn, vn, kc, vc, lens, mode)
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or len(os.sched_getaffinity(0))
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": cores,
-        "kind": "oracle",
-        "sample": f"{rows_done} random query rows of the n=4 L=4096 intra-stream prefill "
-                  f"({rows_done / (c.B * nL * c.Hq):.2%} of all rows), {dt:.1f} s, double-precision C oracle",
-    }
+    ms_full = dt * B / nseq * 1e3
+    return {"value": round(by_total * nseq / B / dt / 1e9, 3), "unit": "GB/s", "ms_extrapolated": round(ms_full, 1),
+            "extrapolated": True, "sample": f"{nseq} of {B} sequences (whole steps), {dt:.1f} s"}
+
+
+def cpu_gather(tabs_host, idsets, reps):
+    """CPU-oracle rate on the expansion gather: the oracle's row copies from
+    host copies of the same tables, over `reps` of the rotating id sets."""
+    import oracle
+
+    ids_host = [ids.cpu().numpy() for ids in idsets[:reps]]
+    oracle.expand_embed(ids_host[0], tabs_host)
+    t0 = time.perf_counter()
+    nbytes = 0
+    for ids in ids_host:
+        out = oracle.expand_embed(ids, tabs_host)
+        nbytes += 2 * out.nbytes + ids.nbytes
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+            "ms_extrapolated": round(dt / len(ids_host) * 1e3, 2), "extrapolated": False,
+            "sample": f"{len(ids_host)} whole calls (rotating id sets), {dt:.2f} s"}
 
 
 def main():
@@ -208,105 +309,33 @@ def main():
     X = synth.CROSS_4K
     Dc = synth.DECODE_8K
     E = synth.EMBED_DECODE
+    EP = synth.EMBED_PREFILL
+    extra_on = not args.no_extra
 
-    comps = {}   # name -> (callable, useful flops, algorithmic bytes)
+    comps = {}    # name -> (callable, useful flops, algorithmic bytes)
+    inputs = {}   # name -> GPU inputs the CPU baseline copies
 
-    def prefill(cfg):
+    def prefill(cfg, name):
         """(callable, useful flops, algorithmic bytes) of one prefill call on
         inputs drawn once; bytes = q, k, v read + o written."""
         q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+        inputs[name] = (q, k, v)
         o = torch.empty_like(q)
         fl = useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
         by = 2 * (2 * q.numel() + k.numel() + v.numel())
         return (lambda: hd.hd_sfa_fwd(q, k, v, o, cfg.n, cfg.mode, cfg.window), fl, by)
 
     if want("intra_n4"):
-        comps["intra_n4"] = prefill(I)
+        comps["intra_n4"] = prefill(I, "intra_n4")
     if want("intra_n1"):
-        comps["intra_n1"] = prefill(I1)
+        comps["intra_n1"] = prefill(I1, "intra_n1")
     if want("cross_n4"):
-        comps["cross_n4"] = prefill(X)
-    def final(cfg):
-        """Final-stream queries (rows t = i*n + n-1 only, compact) of the
-        layer's shapes over K/V of every stream; bytes = q, o of the final
-        stream + the K/V rows the mask reaches (all for cross, stream n-1's
-        for intra)."""
-        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
-        qf = q[:, cfg.n - 1::cfg.n].contiguous()
-        del q
-        o = torch.empty_like(qf)
-        fl = useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
-        kv = (k.numel() + v.numel()) // (cfg.n if cfg.mode == 0 else 1)
-        by = 2 * (2 * qf.numel() + kv)
-        return (lambda: hd.hd_sfa_fwd_final(qf, k, v, o, cfg.n, cfg.mode, cfg.window), fl, by)
-
-    if want("final_cross_n4"):
-        comps["final_cross_n4"] = final(X)
-    if want("final_intra_n4"):
-        comps["final_intra_n4"] = final(I)
-
-    def backward(cfg):
-        """(callable, useful flops, algorithmic bytes) of one backward call of
-        the layer; o and lse come from one forward call outside the timed
-        region, dO is a seeded draw like q, k, v."""
-        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
-        dout = synth.normal(q.shape, 9, cfg.dtype, dev)
-        o, lse = hd.sfa_fwd(q, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(hd.hd_sfa_bwd_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
-                         dtype=torch.uint8, device=dev)
-        # useful FLOPs: five products of the forward's size over the visible
-        # pairs (S recomputed, dP, dV, dK, dQ) = 2.5x the forward's count
-        fl = 2.5 * useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
-        # q, o, dO, k, v read; dq, dk, dv written; lse read, D written and read
-        by = 2 * (4 * q.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.n * cfg.L
-        return (lambda: hd.hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, cfg.n, cfg.mode, cfg.window,
-                                      workspace=ws), fl, by)
-
-    if want("bwd_intra_n4"):
-        comps["bwd_intra_n4"] = backward(I)
-    if want("bwd_intra_n1"):
-        comps["bwd_intra_n1"] = backward(I1)
-    def backward_final(cfg):
-        """Backward of the final-stream queries of the layer (KV-mirror
-        training): dq of the L final rows, dk/dv of all n*L positions."""
-        q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
-        qf = q[:, cfg.n - 1::cfg.n].contiguous()
-        del q
-        dof = synth.normal(qf.shape, 9, cfg.dtype, dev)
-        of, lsef = hd.sfa_fwd_final(qf, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
-        dqf, dkf, dvf = torch.empty_like(qf), torch.empty_like(k), torch.empty_like(v)
-        wsf = torch.empty(hd.hd_sfa_bwd_final_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
-                          dtype=torch.uint8, device=dev)
-        fl = 2.5 * useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
-        by = 2 * (4 * qf.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.L
-        return (lambda: hd.hd_sfa_bwd_final(qf, k, v, of, dof, lsef, dqf, dkf, dvf, cfg.n, cfg.mode, cfg.window,
-                                            workspace=wsf), fl, by)
-
-    if want("bwd_final_cross_n4"):
-        comps["bwd_final_cross_n4"] = backward_final(X)
-    if want("rope_qk"):
-        # rotary embedding of the headline layer's q and k at the expanded
-        # positions (in place); bytes = read + write of q and k
-        q, k, _ = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
-
-        def run_rope(q=q, k=k):
-            hd.hd_rope(q, q, 10000.0)
-            hd.hd_rope(k, k, 10000.0)
-
-        comps["rope_qk"] = (run_rope, 0.0, 2 * 2 * (q.numel() + k.numel()))
-    if want("rope_fwd_intra_n4"):
-        # the headline layer with RoPE fused: k rotated into k_rot, q rotated
-        # inside the prefill kernel (compare rope_qk + intra_n4)
-        q, k, v = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
-        o, k_rot = torch.empty_like(q), torch.empty_like(k)
-        fl = useful_flops(I.B, I.L, I.n, I.Hq, I.d, I.mode, I.window)
-        by = 2 * (2 * q.numel() + 3 * k.numel() + v.numel())
-        comps["rope_fwd_intra_n4"] = (lambda q=q, k=k, v=v, o=o, kr=k_rot: hd.hd_sfa_fwd_rope(q, k, v, o, kr, I.n, I.mode),
-                                      fl, by)
-    if want("decode_intra") or want("decode_cross") or want("decode_final_intra") or want("decode_final_cross"):
+        comps["cross_n4"] = prefill(X, "cross_n4")
+    dec = None
+    if any(want(n) for n in ("decode_intra", "decode_cross", "decode_final_intra", "decode_final_cross")):
         T_cap = Dc.ctx + 8
         dq, dkn, dvn, dkc, dvc = synth.decode_inputs(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap, Dc.dtype, dev)
+        dec = (dq, dkn, dvn, dkc, dvc)
         dcl = torch.full((Dc.B,), Dc.ctx, dtype=torch.int32, device=dev)
         do = torch.empty_like(dq)
         ws = torch.empty(hd.hd_sfa_decode_workspace_bytes(Dc.B, Dc.n, Dc.Hq, Dc.Hkv, Dc.d, T_cap),
@@ -314,34 +343,33 @@ def main():
         # algorithmic bytes: cache read for ctx+1 tokens (the new row from
         # k_new/v_new), q read, o written, new rows written to the cache
         tok_bytes = Dc.n * Dc.Hkv * Dc.d * 2
-        by = 2 * (Dc.ctx * tok_bytes * Dc.B) + 2 * dq.numel() * 2 + 2 * dkn.numel() * 2 * 2
+        dec_by = 2 * (Dc.ctx * tok_bytes * Dc.B) + 2 * dq.numel() * 2 + 2 * dkn.numel() * 2 * 2
         for mode, name in ((0, "decode_intra"), (1, "decode_cross")):
             if want(name):
-                keys = (Dc.ctx + 1) if mode == 0 else None
-                g = Dc.Hq // Dc.Hkv
                 if mode == 0:
-                    pairs = Dc.B * Dc.n * Dc.Hq * keys
+                    pairs = Dc.B * Dc.n * Dc.Hq * (Dc.ctx + 1)
                 else:
                     pairs = Dc.B * Dc.Hq * sum(Dc.ctx * Dc.n + s + 1 for s in range(Dc.n))
-                fl = 4.0 * Dc.d * pairs
                 comps[name] = (lambda mode=mode: hd.hd_sfa_decode(dq, dkn, dvn, dkc, dvc, dcl, do, mode, 0, 0.0, ws),
-                               fl, by)
-                del g
+                               4.0 * Dc.d * pairs, dec_by)
         # KV-mirror layers: the final stream's query only (intra reads stream
         # n-1's cache rows alone, cross the whole cache)
         dqf = dq[:, Dc.n - 1:Dc.n].contiguous()
         dof = torch.empty_like(dqf)
         for mode, name in ((0, "decode_final_intra"), (1, "decode_final_cross")):
-            if want(name):
+            if want(name) and (extra_on or only):
                 rows = Dc.ctx if mode == 0 else Dc.ctx * Dc.n
                 by_f = 2 * rows * Dc.Hkv * Dc.d * 2 * Dc.B + 2 * 2 * dqf.numel() + 2 * dkn.numel() * 2 * 2
                 pairs = Dc.B * Dc.Hq * ((Dc.ctx + 1) if mode == 0 else (Dc.ctx + 1) * Dc.n)
                 comps[name] = (lambda mode=mode: hd.hd_sfa_decode(dqf, dkn, dvn, dkc, dvc, dcl, dof, mode, 0, 0.0, ws,
                                                                   final_only=True), 4.0 * Dc.d * pairs, by_f)
-    if want("embed"):
+    tabs = None
+    if want("embed") or want("embed_prefill"):
         tabs = synth.tables(E["n"], E["V"], E["D"], E["dtype"], dev)
+    if want("embed"):
         # 64 rotating id sets so rows come from HBM rather than the last-level cache
         idsets = [synth.token_ids(E["B"], E["L"], E["V"], seed=1000 + r, device=dev) for r in range(64)]
+        inputs["embed"] = idsets
         eo = torch.empty((E["B"], E["n"] * E["L"], E["D"]), dtype=E["dtype"], device=dev)
         ctr = [0]
 
@@ -349,13 +377,104 @@ def main():
             hd.hd_expand_embed(idsets[ctr[0] % 64], tabs, eo)
             ctr[0] += 1
 
-        by = 2 * eo.numel() * 2 + E["B"] * E["L"] * 4
-        comps["embed"] = (run_embed, 0.0, by)
-    if args.long:
+        comps["embed"] = (run_embed, 0.0, 2 * eo.numel() * 2 + E["B"] * E["L"] * 4)
+    if want("embed_prefill") and (extra_on or only):
+        idsets_p = [synth.token_ids(EP["B"], EP["L"], EP["V"], seed=2000 + r, device=dev) for r in range(64)]
+        inputs["embed_prefill"] = idsets_p
+        epo = torch.empty((EP["B"], EP["n"] * EP["L"], EP["D"]), dtype=EP["dtype"], device=dev)
+        ctrp = [0]
+
+        def run_embed_prefill():
+            hd.hd_expand_embed(idsets_p[ctrp[0] % 64], tabs, epo)
+            ctrp[0] += 1
+
+        comps["embed_prefill"] = (run_embed_prefill, 0.0, 2 * epo.numel() * 2 + EP["B"] * EP["L"] * 4)
+
+    if extra_on or only:
         for cfg, name in ((synth.LONG_INTRA_W, "long_intra_w4096"), (synth.LONG_CROSS_W, "long_cross_w4096"),
                           (synth.LONG_CROSS, "long_cross")):
             if want(name):
-                comps[name] = prefill(cfg)
+                comps[name] = prefill(cfg, name)
+
+        def final(cfg):
+            """Final-stream queries (rows t = i*n + n-1 only, compact) of the
+            layer's shapes over K/V of every stream; bytes = q, o of the final
+            stream + the K/V rows the mask reaches (all for cross, stream n-1's
+            for intra)."""
+            q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+            qf = q[:, cfg.n - 1::cfg.n].contiguous()
+            del q
+            o = torch.empty_like(qf)
+            fl = useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+            kv = (k.numel() + v.numel()) // (cfg.n if cfg.mode == 0 else 1)
+            by = 2 * (2 * qf.numel() + kv)
+            return (lambda: hd.hd_sfa_fwd_final(qf, k, v, o, cfg.n, cfg.mode, cfg.window), fl, by)
+
+        if want("final_cross_n4"):
+            comps["final_cross_n4"] = final(X)
+        if want("final_intra_n4"):
+            comps["final_intra_n4"] = final(I)
+
+        def backward(cfg):
+            """(callable, useful flops, algorithmic bytes) of one backward call of
+            the layer; o and lse come from one forward call outside the timed
+            region, dO is a seeded draw like q, k, v."""
+            q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+            dout = synth.normal(q.shape, 9, cfg.dtype, dev)
+            o, lse = hd.sfa_fwd(q, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = torch.empty(hd.hd_sfa_bwd_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
+                             dtype=torch.uint8, device=dev)
+            # useful FLOPs: five products of the forward's size over the visible
+            # pairs (S recomputed, dP, dV, dK, dQ) = 2.5x the forward's count
+            fl = 2.5 * useful_flops(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+            # q, o, dO, k, v read; dq, dk, dv written; lse read, D written and read
+            by = 2 * (4 * q.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.n * cfg.L
+            return (lambda: hd.hd_sfa_bwd(q, k, v, o, dout, lse, dq, dk, dv, cfg.n, cfg.mode, cfg.window,
+                                          workspace=ws), fl, by)
+
+        if want("bwd_intra_n4"):
+            comps["bwd_intra_n4"] = backward(I)
+        if want("bwd_intra_n1"):
+            comps["bwd_intra_n1"] = backward(I1)
+
+        def backward_final(cfg):
+            """Backward of the final-stream queries of the layer (KV-mirror
+            training): dq of the L final rows, dk/dv of all n*L positions."""
+            q, k, v = synth.qkv(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, cfg.dtype, dev)
+            qf = q[:, cfg.n - 1::cfg.n].contiguous()
+            del q
+            dof = synth.normal(qf.shape, 9, cfg.dtype, dev)
+            of, lsef = hd.sfa_fwd_final(qf, k, v, cfg.n, cfg.mode, cfg.window, return_lse=True)
+            dqf, dkf, dvf = torch.empty_like(qf), torch.empty_like(k), torch.empty_like(v)
+            wsf = torch.empty(hd.hd_sfa_bwd_final_workspace_bytes(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.Hkv, cfg.d),
+                              dtype=torch.uint8, device=dev)
+            fl = 2.5 * useful_flops_final(cfg.B, cfg.L, cfg.n, cfg.Hq, cfg.d, cfg.mode, cfg.window)
+            by = 2 * (4 * qf.numel() + 4 * k.numel()) + 3 * 4 * cfg.B * cfg.Hq * cfg.L
+            return (lambda: hd.hd_sfa_bwd_final(qf, k, v, of, dof, lsef, dqf, dkf, dvf, cfg.n, cfg.mode, cfg.window,
+                                                workspace=wsf), fl, by)
+
+        if want("bwd_final_cross_n4"):
+            comps["bwd_final_cross_n4"] = backward_final(X)
+        if want("rope_qk"):
+            # rotary embedding of the headline layer's q and k at the expanded
+            # positions (in place); bytes = read + write of q and k
+            q, k, _ = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+
+            def run_rope(q=q, k=k):
+                hd.hd_rope(q, q, 10000.0)
+                hd.hd_rope(k, k, 10000.0)
+
+            comps["rope_qk"] = (run_rope, 0.0, 2 * 2 * (q.numel() + k.numel()))
+        if want("rope_fwd_intra_n4"):
+            # the headline layer with RoPE fused: k rotated into k_rot, q rotated
+            # inside the prefill kernel (compare rope_qk + intra_n4)
+            q, k, v = synth.qkv(I.B, I.L, I.n, I.Hq, I.Hkv, I.d, I.dtype, dev)
+            o, k_rot = torch.empty_like(q), torch.empty_like(k)
+            fl = useful_flops(I.B, I.L, I.n, I.Hq, I.d, I.mode, I.window)
+            by = 2 * (2 * q.numel() + 3 * k.numel() + v.numel())
+            comps["rope_fwd_intra_n4"] = (lambda q=q, k=k, v=v, o=o, kr=k_rot:
+                                          hd.hd_sfa_fwd_rope(q, k, v, o, kr, I.n, I.mode), fl, by)
     if "copy" in only:
         # calibration only, never part of the step: a plain elementwise copy
         # of 512 MiB, which reads and writes exactly that many bytes; its HBM
@@ -367,8 +486,8 @@ def main():
 
     # The step is one pass over the hot path's rows (gather, prefill n=4 and
     # the n=1 control, cross layer, decode).  With no --only, the extension
-    # rows (backward, RoPE, final-stream queries) are timed in a loop of their
-    # own after the step, so they neither lengthen nor heat the timed step.
+    # rows are timed in a loop of their own after the step, so they neither
+    # lengthen nor heat the timed step.
     STEP_ROWS = ("intra_n4", "intra_n1", "cross_n4", "decode_intra", "decode_cross", "embed")
     if only:
         step_comps, extra_comps = comps, {}
@@ -409,6 +528,11 @@ def main():
             report[name]["TFLOP/s"] = round(fl / t / 1e9, 2)
         report[name]["GB/s"] = round(by / t / 1e6, 1)
 
+    peaks = None if only else measured_peaks(dev)
+
+    def frac_measured(ach, key):
+        return round(ach / peaks[key], 4) if peaks and peaks.get(key) else None
+
     value = report.get("intra_n4", {}).get("TFLOP/s")
     ratio = None
     if "intra_n4" in report and "intra_n1" in report:
@@ -420,15 +544,55 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic("sfa_fwd_bf16_d128__intra_n4_L4096__hbm_bytes"),
-                "kernel": "sfa_fwd_bf16_d128_kernel", "per_launch_flops": fl}
-    roof_dec = None
-    if "decode_intra" in report:
-        by = comps["decode_intra"][2]
-        ach = by / report["decode_intra"]["ms"] / 1e6
-        roof_dec = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                    "frac": round(ach / PEAK_HBM_GBPS, 4), "per_launch_bytes": by,
-                    "traffic": measured_traffic("sfa_decode_d128__intra_B64_ctx8192__hbm_bytes"),
-                    "kernels": "decode_partial_d128_kernel<1> + decode_combine_kernel<128>"}
+                "kernel": "sfa_fwd_bf16_d128_kernel", "per_launch_flops": fl,
+                "peak_measured": peaks.get("mfma_bf16_TFLOPs") if peaks else None,
+                "frac_measured": frac_measured(ach, "mfma_bf16_TFLOPs")}
+
+    def hbm_roof(name, kernels, traffic_profile):
+        if name not in report:
+            return None
+        by = comps[name][2]
+        ach = by / report[name]["ms"] / 1e6
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "per_launch_bytes": by,
+                "traffic": measured_traffic(traffic_profile), "kernels": kernels,
+                "peak_measured": peaks.get("hbm_read_GBps") if peaks else None,
+                "frac_measured": frac_measured(ach, "hbm_read_GBps")}
+
+    roof_dec = hbm_roof("decode_intra", "decode_partial_d128_kernel<1> + decode_combine_kernel<128>",
+                        "sfa_decode_d128__intra_B64_ctx8192__hbm_bytes")
+    roof_emb = hbm_roof("embed_prefill", "expand_embed_rows", "expand_embed__prefill_16384_rows__hbm_bytes")
+
+    cpu = None
+    cpu_rows = None
+    if not args.no_cpu and not only:
+        budget = args.cpu_seconds
+        cpu_rows = {}
+        share = {"intra_n4": 0.2, "intra_n1": 0.12, "cross_n4": 0.16, "long_intra_w4096": 0.12,
+                 "long_cross": 0.12}
+        for name, cfg in (("intra_n4", I), ("intra_n1", I1), ("cross_n4", X),
+                          ("long_intra_w4096", synth.LONG_INTRA_W), ("long_cross", synth.LONG_CROSS)):
+            if name in inputs:
+                cpu_rows[name] = cpu_prefill(cfg, budget * share[name], seed=123, gpu_inputs=inputs[name])
+        if dec is not None:
+            for mode, name in ((0, "decode_intra"), (1, "decode_cross")):
+                cpu_rows[name] = cpu_decode(*dec, Dc.ctx, mode, 8 if mode == 0 else 4, comps[name][2])
+        if tabs is not None and ("embed" in inputs or "embed_prefill" in inputs):
+            tabs_host = [t.cpu() for t in tabs]
+            if "embed" in inputs:
+                cpu_rows["embed"] = cpu_gather(tabs_host, inputs["embed"], 64)
+            if "embed_prefill" in inputs:
+                cpu_rows["embed_prefill"] = cpu_gather(tabs_host, inputs["embed_prefill"], 4)
+            del tabs_host
+        for name, row in cpu_rows.items():
+            row["cores"] = _cores()
+            if name in report:
+                row["gpu_speedup"] = round(row["ms_extrapolated"] / report[name]["ms"], 1)
+        head = cpu_rows.get("intra_n4")
+        if head is not None:
+            cpu = {"value": head["value"], "unit": head["unit"], "cores": _cores(), "kind": "oracle",
+                   "sample": head["sample"] + " of the n=4 L=4096 intra-stream prefill, double-precision C oracle, "
+                             "rate extrapolated to the whole layer"}
 
     line = {
         "metric": "stream-factorized attn TFLOP/s (useful) at n=4 + n4/n1 time ratio; decode GB/s",
@@ -459,8 +623,13 @@ def main():
         "step_components": list(step_comps),
         "roofline": roof,
         "roofline_decode": roof_dec,
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(args.cpu_seconds),
-        "measured_peaks": None if only else measured_peaks(dev),
+        "roofline_embed": roof_emb,
+        "cpu_baseline": cpu,
+        "cpu_baseline_rows": cpu_rows,
+        "cpu_n4_n1_time_ratio": (round(cpu_rows["intra_n4"]["ms_extrapolated"] /
+                                       cpu_rows["intra_n1"]["ms_extrapolated"], 3)
+                                 if cpu_rows and "intra_n4" in cpu_rows and "intra_n1" in cpu_rows else None),
+        "measured_peaks": peaks,
     }
     print(json.dumps(line), flush=True)
 

@@ -34,8 +34,12 @@
  * HD_ERR_DEVICE: the HIP runtime reported an error at launch.  On any non-OK
  * return nothing was launched by that call (except HD_ERR_DEVICE, where an
  * earlier kernel of the same call may have been enqueued) and hd_last_error()
- * describes the problem.  Token ids outside [0,V) and cache_len[b] >= T_cap are
- * caller contract violations that the device code does not check.
+ * describes the problem.  Token ids outside [0,V) and cache_len[b] outside
+ * [0, T_cap) are caller contract violations: the host cannot see device
+ * values without synchronising, so they are not validated here (the Python
+ * binding checks both when HD_DEBUG=1).  On the device, a decode step skips a
+ * sequence whose cache_len is out of range (no append, no cache read) and
+ * writes NaN to its outputs; an out-of-range id reads row min(max(id,0),V-1).
  */
 #ifndef HD_H
 #define HD_H

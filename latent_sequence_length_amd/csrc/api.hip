@@ -100,6 +100,7 @@ hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n, const void *c
     a.B = B;
     a.L = L;
     a.n = n;
+    a.V = V;
     a.row_bytes = (int64_t)D * (dt == HD_BF16 ? 2 : 4);
     return device_status(hd::launch_expand_embed(a, static_cast<hipStream_t>(stream)), "expand_embed launch");
 }

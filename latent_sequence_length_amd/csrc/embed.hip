@@ -2,10 +2,19 @@
 // "Multi-Stream Expansion and Training Objective": S_t = E_k(x_i) at expanded
 // position t = (i-1)n + k, here 0-based t = i*n + s).
 //
-// A pure HBM stream: every output row is a byte copy of one table row.  One
-// wavefront copies one row with 16-byte lane accesses (a 14 KB bf16 row of
-// dim 7168 is 14 fully coalesced 1 KB wave transactions); a workgroup of four
-// waves handles four rows at a time and strides over the grid.
+// A pure HBM stream: every output row is a byte copy of one table row, read
+// from a random place in a multi-GB table and written contiguously.
+//   * rows of >= 4 KB (the 14 KB bf16 rows of dim 7168): a workgroup of 256
+//     lanes copies up to 16 KB of one row -- each lane issues its four 16-byte
+//     loads before any store, so a CU with eight such workgroups keeps
+//     ~128 KB of reads in flight; the row, its token id and its table are
+//     wave-uniform (scalar) and only the in-row offset is per lane.  Table
+//     rows are read with non-temporal loads (they are not reused) and the
+//     output rows written with non-temporal stores (the next layer reads them
+//     long after this kernel, so they should not displace L2 lines);
+//   * shorter rows: one wavefront per row, 16-byte (or 2-byte) lane accesses.
+// An id outside [0, V) breaks the caller's contract; it is clamped to the
+// table so that no read leaves it.
 #include "hd_internal.h"
 
 namespace hd {
@@ -13,6 +22,37 @@ namespace hd {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kChunkVec = 1024;  // 16-byte vectors per workgroup of the row-chunk kernel (16 KB)
+constexpr int kPerLane = kChunkVec / 256;
+
+__device__ __forceinline__ int64_t clamp_id(int64_t id, int64_t V) { return id < 0 ? 0 : (id >= V ? V - 1 : id); }
+
+__global__ __launch_bounds__(256) void expand_embed_rows(EmbedArgs a, int nchunk) {
+    const int tid = threadIdx.x;
+    const int64_t wg = blockIdx.x;
+    const int64_t r = wg / nchunk;                 // output row (b, i, s), wave-uniform
+    const int chunk = (int)(wg - r * nchunk);
+    const int Ln = a.L * a.n;
+    const int b = (int)(r / Ln);
+    const int rem = (int)(r - (int64_t)b * Ln);
+    const int i = rem / a.n, s = rem - i * a.n;
+    const int64_t id = clamp_id(a.ids[(int64_t)b * a.L + i], a.V);
+    const int nvec = (int)(a.row_bytes >> 4);
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.tables[s] + id * a.row_bytes);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + r * a.row_bytes);
+    const int c0 = chunk * kChunkVec + tid;
+    u32x4 x[kPerLane];
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+        const int c = c0 + 256 * u;
+        if (c < nvec) x[u] = __builtin_nontemporal_load(src + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kPerLane; ++u) {
+        const int c = c0 + 256 * u;
+        if (c < nvec) __builtin_nontemporal_store(x[u], dst + c);
+    }
+}
 
 __global__ __launch_bounds__(256) void expand_embed_v16(EmbedArgs a, int64_t nrows) {
     const int lane = threadIdx.x & 63;
@@ -23,24 +63,15 @@ __global__ __launch_bounds__(256) void expand_embed_v16(EmbedArgs a, int64_t nro
         const int b = (int)(r / Ln);
         const int rem = (int)(r - (int64_t)b * Ln);
         const int i = rem / a.n, s = rem - i * a.n;
-        const int64_t id = a.ids[(int64_t)b * a.L + i];
+        const int64_t id = clamp_id(a.ids[(int64_t)b * a.L + i], a.V);
         const u32x4 *src = reinterpret_cast<const u32x4 *>(a.tables[s] + id * a.row_bytes);
         u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + r * a.row_bytes);
-        int64_t c = lane;
-        // Four independent 16-byte loads in flight per lane before the stores.
-        for (; c + 192 < nvec; c += 256) {
-            u32x4 x0 = __builtin_nontemporal_load(src + c);
-            u32x4 x1 = __builtin_nontemporal_load(src + c + 64);
-            u32x4 x2 = __builtin_nontemporal_load(src + c + 128);
-            u32x4 x3 = __builtin_nontemporal_load(src + c + 192);
-            dst[c] = x0; dst[c + 64] = x1; dst[c + 128] = x2; dst[c + 192] = x3;
-        }
-        for (; c < nvec; c += 64) dst[c] = __builtin_nontemporal_load(src + c);
+        for (int64_t c = lane; c < nvec; c += 64) dst[c] = __builtin_nontemporal_load(src + c);
     }
 }
 
-// Fallback for rows whose size is not a multiple of 16 bytes: 2-byte units
-// (every supported dtype is 2 or 4 bytes wide).
+// Rows whose size is not a multiple of 16 bytes: 2-byte units (every
+// supported dtype is 2 or 4 bytes wide).
 __global__ __launch_bounds__(256) void expand_embed_u16(EmbedArgs a, int64_t nrows) {
     const int lane = threadIdx.x & 63;
     const int64_t wave0 = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -50,7 +81,7 @@ __global__ __launch_bounds__(256) void expand_embed_u16(EmbedArgs a, int64_t nro
         const int b = (int)(r / Ln);
         const int rem = (int)(r - (int64_t)b * Ln);
         const int i = rem / a.n, s = rem - i * a.n;
-        const int64_t id = a.ids[(int64_t)b * a.L + i];
+        const int64_t id = clamp_id(a.ids[(int64_t)b * a.L + i], a.V);
         const uint16_t *src = reinterpret_cast<const uint16_t *>(a.tables[s] + id * a.row_bytes);
         uint16_t *dst = reinterpret_cast<uint16_t *>(a.out + r * a.row_bytes);
         for (int64_t c = lane; c < nunit; c += 64) dst[c] = src[c];
@@ -61,6 +92,13 @@ __global__ __launch_bounds__(256) void expand_embed_u16(EmbedArgs a, int64_t nro
 
 hipError_t launch_expand_embed(const EmbedArgs &a, hipStream_t st) {
     const int64_t nrows = (int64_t)a.B * a.L * a.n;
+    if (a.row_bytes % 16 == 0 && a.row_bytes >= 4096) {
+        const int nchunk = (int)((a.row_bytes / 16 + kChunkVec - 1) / kChunkVec);
+        const int64_t grid = nrows * nchunk;
+        if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(expand_embed_rows, dim3((unsigned)grid), dim3(256), 0, st, a, nchunk);
+        return hipGetLastError();
+    }
     int64_t blocks = (nrows + kWaves - 1) / kWaves;
     if (blocks > 65536) blocks = 65536;
     if (a.row_bytes % 16 == 0)

@@ -24,6 +24,7 @@ struct EmbedArgs {
     const char *tables[16];
     char *out;
     int B, L, n;
+    int64_t V;          // rows per table (ids are clamped to [0, V))
     int64_t row_bytes;
 };
 hipError_t launch_expand_embed(const EmbedArgs &a, hipStream_t st);

@@ -27,16 +27,13 @@
 
 #include "attn_common.h"
 
-#ifndef HD_DECODE_NBUF
-#define HD_DECODE_NBUF 4      // tile buffers (copies run NBUF-1 tiles ahead)
-#endif
-#ifndef HD_DECODE_TARGET_WGS
-#define HD_DECODE_TARGET_WGS 1024  // workgroups the d=128 split aims for
-#endif
-
 namespace hd {
 
 namespace {
+
+// Workgroups the d=128 split aims for (one per CU at a time; 512-1024 measured
+// best at B=64, ctx 8192: fewer leave HBM idle, more pay start-up latency).
+constexpr int kDecodeTargetWgs = 1024;
 
 constexpr int NW = 4;    // waves per workgroup
 constexpr int RB = 32;   // cache rows per wave block
@@ -52,7 +49,7 @@ struct Split {
 
 bool use_d128_path(int n, int d) { return d == 128 && 64 % n == 0; }
 
-Split choose_split_d128(int B, int Hkv, int T_cap, int target = HD_DECODE_TARGET_WGS) {
+Split choose_split_d128(int B, int Hkv, int T_cap, int target = kDecodeTargetWgs) {
     // One workgroup per CU (128 KB LDS): aim for ~target workgroups, chunks
     // of >= 64 tokens in multiples of 16.
     const int64_t bh = (int64_t)B * Hkv;
@@ -93,6 +90,9 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
     const int n = p.n, g = p.Hq / p.Hkv, QR = p.nqs * g;
     const int len = p.cache_len[b];
     const int c0 = split * sp.chunk;
+    // a length outside [0, T_cap) breaks the caller's contract: no append, no
+    // scan (the combine writes NaN rows for that sequence)
+    if (len < 0 || len >= p.T_cap) return;
     if (c0 > len) return;  // nothing cached here yet; the combine skips it
     const int c1 = min(c0 + sp.chunk, len + 1);
 
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecArgs p, Split sp
 //   LDS rows are 256 B with the chunk swizzle sw(r) used by the prefill.
 constexpr int DT_ROWS = 64;                    // cache rows per tile
 constexpr int DT_TILE = DT_ROWS * 128 * 2;     // bytes of one K (or V) tile
-constexpr int DT_NBUF = HD_DECODE_NBUF;
+constexpr int DT_NBUF = 4;                   // tile buffers: copies run three tiles ahead
 static_assert(DT_NBUF >= 2 && DT_NBUF <= 5, "tile buffers");
 
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
@@ -336,6 +336,9 @@ __global__ __launch_bounds__(256, 1) void decode_partial_d128_kernel(DecArgs p, 
     const int n = p.n, g = p.Hq / p.Hkv, QR = p.nqs * g;
     const int len = p.cache_len[b];
     const int c0 = split * sp.chunk;
+    // a length outside [0, T_cap) breaks the caller's contract: no append, no
+    // scan (the combine writes NaN rows for that sequence)
+    if (len < 0 || len >= p.T_cap) return;
     if (c0 > len) return;  // nothing cached here yet; the combine skips it
     const int c1 = min(c0 + sp.chunk, len + 1);
 
@@ -566,6 +569,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp
     const int bh = (int)(row / QR);
     const int b = bh / p.Hkv, kvh = bh - b * p.Hkv;
     const int len = p.cache_len[b];
+    const int sr = c / g, hh = c - sr * g;  // query stream qs0 + sr
+    bf16 *op = static_cast<bf16 *>(p.o) + (((int64_t)b * p.nqs + sr) * p.Hq + kvh * g + hh) * D;
+    constexpr int PER = (D + 63) / 64;
+    if (len < 0 || len >= p.T_cap) {  // contract violation: no partial was written
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int dim = lane + 64 * e;
+            if (dim < D) reinterpret_cast<unsigned short *>(op)[dim] = 0x7fc0;  // bf16 quiet NaN
+        }
+        return;
+    }
     const int ns = min(sp.nsplit, len / sp.chunk + 1);  // splits with c0 <= len
     const float *ws_acc = p.ws;
     const float *ws_ml = p.ws + (int64_t)p.B * p.Hkv * sp.nsplit * QR * D;
@@ -573,7 +587,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp
 
     float M = -INFINITY;
     for (int k = 0; k < ns; ++k) M = fmaxf(M, ws_ml[(part0 + (int64_t)k * QR) * 2]);
-    constexpr int PER = (D + 63) / 64;
     float acc[PER] = {};
     float L = 0.f;
     for (int k = 0; k < ns; ++k) {
@@ -586,8 +599,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecArgs p, Split sp
             if (dim < D) acc[e] += wt * ws_acc[pk * D + dim];
         }
     }
-    const int sr = c / g, hh = c - sr * g;  // query stream qs0 + sr
-    bf16 *op = static_cast<bf16 *>(p.o) + (((int64_t)b * p.nqs + sr) * p.Hq + kvh * g + hh) * D;
     const float inv = 1.f / L;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
@@ -653,7 +664,7 @@ hipError_t launch_sfa_decode_bf16(const DecArgs &a, hipStream_t st) {
         // a scan of one stream's rows (rpt = 1 of n) reads 1/n of the bytes
         // per token: fewer, longer chunks (sweep: B=64, ctx 8192, final-stream
         // intra decode 0.371 ms at 1024 workgroups, 0.357 ms at 512)
-        const Split sp = choose_split_d128(a.B, a.Hkv, a.T_cap, std::max(1, HD_DECODE_TARGET_WGS * a.rpt / a.n));
+        const Split sp = choose_split_d128(a.B, a.Hkv, a.T_cap, std::max(1, kDecodeTargetWgs * a.rpt / a.n));
         const int QR = a.nqs * (a.Hq / a.Hkv);
         hipError_t e;
         switch ((QR + 15) / 16) {

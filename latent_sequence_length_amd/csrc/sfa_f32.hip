@@ -81,6 +81,12 @@ __global__ __launch_bounds__(64) void sfa_decode_f32_kernel(DecArgs p) {
     const int b = (int)(row / p.Hq / p.nqs);
     const int g = p.Hq / p.Hkv, kvh = h / g;
     const int len = p.cache_len[b];
+    if (len < 0 || len >= p.T_cap) {  // contract violation: NaN row, nothing read
+        float *op = static_cast<float *>(p.o) + row * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) reinterpret_cast<unsigned *>(op)[c] = 0x7fc00000u;  // quiet NaN
+        return;
+    }
     const float *qg = static_cast<const float *>(p.q);
     const float *kn = static_cast<const float *>(p.k_new);
     const float *vn = static_cast<const float *>(p.v_new);
@@ -137,7 +143,9 @@ __global__ __launch_bounds__(256) void append_f32_kernel(DecArgs p) {
     if (idx >= per_b * p.B) return;
     const int b = (int)(idx / per_b);
     const int64_t e = idx - (int64_t)b * per_b;
-    const int64_t dst = ((int64_t)b * p.T_cap + p.cache_len[b]) * per_b + e;
+    const int len = p.cache_len[b];
+    if (len < 0 || len >= p.T_cap) return;  // contract violation: the cache is left as it is
+    const int64_t dst = ((int64_t)b * p.T_cap + len) * per_b + e;
     static_cast<float *>(p.k_cache)[dst] = static_cast<const float *>(p.k_new)[idx];
     static_cast<float *>(p.v_cache)[dst] = static_cast<const float *>(p.v_new)[idx];
 }

@@ -4,6 +4,12 @@ Argument marshalling only: every step runs in the library's HIP kernels.
 PyTorch supplies device memory and the current HIP stream.  There is no
 fallback: if ``libhd.so`` is absent or a tensor is not on the GPU, the call
 raises.
+
+Debug mode (environment variable ``HD_DEBUG=1``): the two caller contracts
+the C ABI cannot check without synchronising -- token ids in [0, V) for the
+expansion, ``cache_len[b]`` in [0, T_cap) for a decode step -- are checked
+here before anything is launched (one device-to-host read each), raising
+ValueError.
 """
 import ctypes
 import os
@@ -73,6 +79,28 @@ def last_error():
     return load().hd_last_error().decode()
 
 
+def debug_enabled():
+    """True when HD_DEBUG=1: the wrapper checks ids and cache lengths."""
+    return os.environ.get("HD_DEBUG", "") == "1"
+
+
+def _debug_check_ids(ids, V):
+    """Every id in [0, V) (debug mode only; reads ids back to the host)."""
+    if ids.numel() == 0:
+        return
+    lo, hi = int(ids.min()), int(ids.max())
+    if lo < 0 or hi >= V:
+        raise ValueError(f"token ids must lie in [0, {V}); found min {lo}, max {hi}")
+
+
+def _debug_check_lens(cache_len, T_cap):
+    """Every cache_len[b] in [0, T_cap) (debug mode only)."""
+    lo, hi = int(cache_len.min()), int(cache_len.max())
+    if lo < 0 or hi >= T_cap:
+        raise ValueError(f"cache_len must lie in [0, T_cap={T_cap}) so the new token fits; "
+                         f"found min {lo}, max {hi}")
+
+
 def _check(status):
     if status != HD_OK:
         raise HDError(status, last_error())
@@ -114,6 +142,8 @@ def hd_expand_embed(ids, tables, out):
             raise ValueError("tables must share shape and dtype")
     if out.shape != (B, n * L, D) or out.dtype != tables[0].dtype:
         raise ValueError(f"out must be {(B, n * L, D)} of {tables[0].dtype}")
+    if debug_enabled():
+        _debug_check_ids(ids, V)
     ptrs = (ctypes.c_void_p * n)(*[_dev(t, f"tables[{s}]") for s, t in enumerate(tables)])
     _check(load().hd_expand_embed(_dev(ids, "ids", torch.int32), B, L, n, ptrs, V, D,
                                   _dtype_code(tables[0]), _dev(out, "out"), _stream(out)))
@@ -192,11 +222,8 @@ def hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap):
     return int(load().hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap))
 
 
-def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=0, scale=0.0,
-                  workspace=None, final_only=False):
-    """One decode step: append k_new/v_new at cache_len, attend, write o.
-    final_only: q and o are [B, 1, Hq, d], the final stream's query of a
-    KV-mirror layer (hd_sfa_decode_final)."""
+def _decode_shapes(q, k_new, v_new, k_cache, v_cache, cache_len, o, final_only):
+    """Validate the decode tensors; returns (B, n, Hq, Hkv, d, T_cap, dtype code)."""
     B, nq, Hq, d = q.shape
     n = k_new.shape[1]
     if nq != (1 if final_only else n):
@@ -213,6 +240,17 @@ def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=
     for t, name in ((k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache"), (o, "o")):
         if t.dtype != q.dtype:
             raise TypeError(f"{name} dtype {t.dtype} differs from q's {q.dtype}")
+    if debug_enabled():
+        _debug_check_lens(cache_len, T_cap)
+    return B, n, Hq, Hkv, d, T_cap, dt
+
+
+def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=0, scale=0.0,
+                  workspace=None, final_only=False):
+    """One decode step: append k_new/v_new at cache_len, attend, write o.
+    final_only: q and o are [B, 1, Hq, d], the final stream's query of a
+    KV-mirror layer (hd_sfa_decode_final)."""
+    B, n, Hq, Hkv, d, T_cap, dt = _decode_shapes(q, k_new, v_new, k_cache, v_cache, cache_len, o, final_only)
     need = hd_sfa_decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap)
     if workspace is None and dt == HD_BF16:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

@@ -254,3 +254,71 @@ def test_binding_refuses_cpu_tensors(lib):
     q = torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         hd.sfa_fwd(q, q, q, 2, 0)
+
+
+# ---------------------------------------------------------------------------
+# Debug mode of the binding (HD_DEBUG=1): the two caller contracts the C ABI
+# does not check on the host -- ids in [0, V), cache_len in [0, T_cap) -- are
+# checked before anything reaches the library.  The tensors here live on the
+# CPU: with the contract broken the wrapper raises ValueError before it looks
+# at the device; with it kept, the call gets as far as the GPU-tensor check.
+# ---------------------------------------------------------------------------
+
+def _embed_args(ids):
+    tabs = [torch.zeros(10, 8, dtype=torch.bfloat16) for _ in range(2)]
+    out = torch.empty(ids.shape[0], 2 * ids.shape[1], 8, dtype=torch.bfloat16)
+    return ids, tabs, out
+
+
+@pytest.mark.parametrize("bad", [-1, 10, 1 << 20])
+def test_debug_mode_rejects_ids_outside_the_table(monkeypatch, bad):
+    monkeypatch.setenv("HD_DEBUG", "1")
+    ids = torch.tensor([[0, 3, bad, 9]], dtype=torch.int32)
+    with pytest.raises(ValueError, match=r"\[0, 10\)"):
+        hd.hd_expand_embed(*_embed_args(ids))
+
+
+def test_debug_mode_passes_valid_ids_on(monkeypatch):
+    monkeypatch.setenv("HD_DEBUG", "1")
+    ids = torch.tensor([[0, 3, 9, 9]], dtype=torch.int32)
+    with pytest.raises(TypeError, match="GPU tensor"):
+        hd.hd_expand_embed(*_embed_args(ids))
+
+
+def test_debug_mode_off_by_default(monkeypatch):
+    monkeypatch.delenv("HD_DEBUG", raising=False)
+    ids = torch.tensor([[0, 3, 77, 9]], dtype=torch.int32)
+    with pytest.raises(TypeError, match="GPU tensor"):  # no id check without debug mode
+        hd.hd_expand_embed(*_embed_args(ids))
+
+
+def _decode_args(lens, T_cap=16):
+    B, n, Hq, Hkv, d = len(lens), 2, 4, 2, 32
+    q = torch.zeros(B, n, Hq, d, dtype=torch.bfloat16)
+    kn = torch.zeros(B, n, Hkv, d, dtype=torch.bfloat16)
+    kc = torch.zeros(B, T_cap, n, Hkv, d, dtype=torch.bfloat16)
+    cl = torch.tensor(lens, dtype=torch.int32)
+    return q, kn, kn.clone(), kc, kc.clone(), cl, torch.empty_like(q)
+
+
+@pytest.mark.parametrize("lens", [[3, 16], [-1, 0], [15, 40]])
+@pytest.mark.parametrize("entry", ["hd_sfa_decode"])
+def test_debug_mode_rejects_cache_len_outside_the_cache(monkeypatch, lens, entry):
+    monkeypatch.setenv("HD_DEBUG", "1")
+    with pytest.raises(ValueError, match="T_cap=16"):
+        getattr(hd, entry)(*_decode_args(lens), 0)
+
+
+def test_debug_mode_rejects_cache_len_of_final_stream_decode(monkeypatch):
+    monkeypatch.setenv("HD_DEBUG", "1")
+    q, kn, vn, kc, vc, cl, _ = _decode_args([2, 16])
+    qf = q[:, 1:].contiguous()
+    with pytest.raises(ValueError, match="T_cap=16"):
+        hd.hd_sfa_decode(qf, kn, vn, kc, vc, cl, torch.empty_like(qf), 1, final_only=True)
+
+
+@pytest.mark.parametrize("entry", ["hd_sfa_decode"])
+def test_debug_mode_passes_valid_cache_len_on(monkeypatch, entry):
+    monkeypatch.setenv("HD_DEBUG", "1")
+    with pytest.raises(TypeError, match="GPU tensor"):
+        getattr(hd, entry)(*_decode_args([0, 15]), 0)
