@@ -16,7 +16,8 @@
  *   - Every tensor pointer is DEVICE memory owned by the caller, row-major and
  *     dense, 16-byte aligned.  The library allocates no memory, keeps no
  *     pointer after a call returns and holds no state between calls except a
- *     thread-local error string.
+ *     thread-local error string (and the static scratch array of
+ *     hd_sfa_decode_noalloc).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns without synchronising; results
  *     are deterministic (no atomics, fixed reduction orders).
@@ -272,6 +273,23 @@ hd_status hd_sfa_decode_final(const void *q, const void *k_new, const void *v_ne
                               const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
                               hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/*
+ * hd_sfa_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, semantics and errors as hd_sfa_decode, without the
+ * workspace: the split-KV partials go to a scratch array of
+ * HD_NOALLOC_SCRATCH_BYTES that the library holds in device memory, one copy
+ * per GPU, from the first call on that GPU until the process ends.  Sizes
+ * whose partials need more (hd_sfa_decode_workspace_bytes above the limit)
+ * return HD_ERR_INVALID.  The call allocates nothing.  Calls that overlap on
+ * one GPU (enqueued on different streams without ordering between them) race
+ * on the shared scratch; calls ordered on one stream do not.
+ */
+#define HD_NOALLOC_SCRATCH_BYTES (32u << 20)
+hd_status hd_sfa_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                                hd_mode mode, int window, float scale, hd_dtype dt, void *stream);
 
 /* Static name of a status code. */
 const char *hd_status_string(hd_status s);

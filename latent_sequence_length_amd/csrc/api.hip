@@ -1,11 +1,13 @@
 // api.hip -- the C ABI of libhd.so (declared in include/hd.h): argument
 // validation on the host, then dispatch to the HIP kernels on the caller's
-// stream.  No allocation, no synchronisation, no state beyond a thread-local
-// error string.
+// stream.  No allocation, no synchronisation; the only state is a
+// thread-local error string and, for the allocation-free decode entry point,
+// the per-device address of its static scratch array.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "hd.h"
 #include "hd_internal.h"
@@ -61,6 +63,35 @@ hd_status check_attn(int B, int n, int Hq, int Hkv, int d, int mode, int window,
 
 float resolve_scale(float scale, int d) {
     return (scale > 0.f && std::isfinite(scale)) ? scale : 1.0f / std::sqrt((float)d);
+}
+
+// Scratch of hd_sfa_decode_noalloc: the split-KV partials of one decode step
+// live here instead of in a caller workspace.  One copy per GPU the library
+// runs on, held until the process ends; every call on a GPU shares it.
+static __device__ __align__(256) char scratch[HD_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` per device, looked up once per device (with it
+// current) on the first allocation-free call there.  Host code never uses the
+// array's own name as an address: on the host it is only a stand-in symbol.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hd_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(HD_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(HD_ERR_UNSUPPORTED, "device %d above %d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr)
+            return fail(HD_ERR_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return HD_OK;
 }
 
 }  // namespace
@@ -320,7 +351,8 @@ size_t hd_sfa_decode_workspace_bytes(int B, int n, int Hq, int Hkv, int d, int T
 static hd_status sfa_decode_common(const void *q, const void *k_new, const void *v_new, void *k_cache,
                                    void *v_cache, const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq,
                                    int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt,
-                                   void *workspace, size_t workspace_bytes, void *stream, bool final_only) {
+                                   void *workspace, size_t workspace_bytes, void *stream, bool final_only,
+                                   bool noalloc = false) {
     HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
     if (T_cap < 1) return fail(HD_ERR_INVALID, "T_cap=%d < 1", T_cap);
     const int qrows = (final_only ? 1 : n) * (Hq / Hkv);
@@ -348,6 +380,14 @@ static hd_status sfa_decode_common(const void *q, const void *k_new, const void 
     const char *what = final_only ? "sfa_decode_final launch" : "sfa_decode launch";
     if (dt == HD_BF16) {
         const size_t need = hd::decode_workspace_bytes(B, n, Hq, Hkv, d, T_cap);
+        if (noalloc) {  // the library's own scratch, looked up after every other check
+            if (need > (size_t)HD_NOALLOC_SCRATCH_BYTES)
+                return fail(HD_ERR_INVALID, "these sizes need %zu bytes of split-KV scratch, above the %zu bytes "
+                            "hd_sfa_decode_noalloc holds (use hd_sfa_decode with a workspace)",
+                            need, (size_t)HD_NOALLOC_SCRATCH_BYTES);
+            HD_TRY(scratch_for_current_device(&workspace));
+            workspace_bytes = (size_t)HD_NOALLOC_SCRATCH_BYTES;
+        }
         if (workspace_bytes < need)
             return fail(HD_ERR_INVALID, "workspace of %zu bytes below the %zu required", workspace_bytes, need);
         HD_TRY(check_ptr(workspace, "workspace"));
@@ -363,6 +403,13 @@ hd_status hd_sfa_decode(const void *q, const void *k_new, const void *v_new, voi
                         size_t workspace_bytes, void *stream) {
     return sfa_decode_common(q, k_new, v_new, k_cache, v_cache, cache_len, T_cap, o, B, n, Hq, Hkv, d, mode, window,
                              scale, dt, workspace, workspace_bytes, stream, false);
+}
+
+hd_status hd_sfa_decode_noalloc(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                                const int32_t *cache_len, int T_cap, void *o, int B, int n, int Hq, int Hkv, int d,
+                                hd_mode mode, int window, float scale, hd_dtype dt, void *stream) {
+    return sfa_decode_common(q, k_new, v_new, k_cache, v_cache, cache_len, T_cap, o, B, n, Hq, Hkv, d, mode, window,
+                             scale, dt, nullptr, 0, stream, false, true);
 }
 
 hd_status hd_sfa_decode_final(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,

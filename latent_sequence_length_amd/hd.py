@@ -51,6 +51,7 @@ def load():
     lib.hd_sfa_decode_workspace_bytes.restype = SZ
     lib.hd_sfa_decode.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_sfa_decode_final.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P, SZ, P]
+    lib.hd_sfa_decode_noalloc.argtypes = [P, P, P, P, P, P, I, P, I, I, I, I, I, I, I, F, I, P]
     lib.hd_sfa_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.hd_sfa_bwd_workspace_bytes.restype = SZ
     lib.hd_sfa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
@@ -59,7 +60,7 @@ def load():
     lib.hd_sfa_bwd_final.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I, P, SZ, P]
     lib.hd_rope.argtypes = [P, P, I, I, I, I, P, I64, I64, I64, F, I, P]
     for f in (lib.hd_expand_embed, lib.hd_sfa_fwd, lib.hd_sfa_fwd_final, lib.hd_sfa_fwd_rope, lib.hd_sfa_decode,
-              lib.hd_sfa_decode_final, lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
+              lib.hd_sfa_decode_final, lib.hd_sfa_decode_noalloc, lib.hd_sfa_bwd, lib.hd_sfa_bwd_final, lib.hd_rope):
         f.restype = ctypes.c_int
     lib.hd_status_string.argtypes = [I]
     lib.hd_status_string.restype = ctypes.c_char_p
@@ -262,6 +263,17 @@ def hd_sfa_decode(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=
                  _dev(cache_len, "cache_len", torch.int32), T_cap, _dev(o, "o"),
                  B, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt,
                  wp, wbytes, _stream(q)))
+    return o
+
+
+def hd_sfa_decode_noalloc(q, k_new, v_new, k_cache, v_cache, cache_len, o, mode, window=0, scale=0.0):
+    """hd_sfa_decode without a workspace: the library's own per-GPU scratch
+    holds the split-KV partials (HD_NOALLOC_SCRATCH_BYTES at most)."""
+    B, n, Hq, Hkv, d, T_cap, dt = _decode_shapes(q, k_new, v_new, k_cache, v_cache, cache_len, o, False)
+    _check(load().hd_sfa_decode_noalloc(_dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"),
+                                        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                        _dev(cache_len, "cache_len", torch.int32), T_cap, _dev(o, "o"),
+                                        B, n, Hq, Hkv, d, int(mode), int(window), float(scale), dt, _stream(q)))
     return o
 
 

@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
         "hd_expand_embed", "hd_rope", "hd_sfa_fwd", "hd_sfa_fwd_final", "hd_sfa_fwd_rope",
         "hd_sfa_bwd_workspace_bytes", "hd_sfa_bwd",
         "hd_sfa_bwd_final_workspace_bytes", "hd_sfa_bwd_final",
-        "hd_sfa_decode_workspace_bytes", "hd_sfa_decode", "hd_sfa_decode_final",
+        "hd_sfa_decode_workspace_bytes", "hd_sfa_decode", "hd_sfa_decode_final", "hd_sfa_decode_noalloc",
         "hd_status_string", "hd_last_error", "hd_version"])
 
 
@@ -128,6 +128,22 @@ def test_decode_final_validation(lib, kw, code):
              workspace=FAKE, workspace_bytes=0, stream=None)
     a.update(kw)
     assert lib.hd_sfa_decode_final(*a.values()) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T_cap=0), hd.HD_ERR_INVALID), (dict(B=0), hd.HD_ERR_INVALID), (dict(Hq=6, Hkv=4), hd.HD_ERR_INVALID),
+    (dict(cache_len=None), hd.HD_ERR_INVALID), (dict(d=48), hd.HD_ERR_UNSUPPORTED),
+    (dict(n=8, Hq=32, Hkv=2), hd.HD_ERR_UNSUPPORTED),
+    # 1024 sequences need 68 MB of split-KV partials, above the 32 MiB scratch
+    (dict(B=1024, n=4, Hq=32, Hkv=8, T_cap=64), hd.HD_ERR_INVALID),
+])
+def test_decode_noalloc_validation(lib, kw, code):
+    a = dict(q=FAKE, k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, cache_len=FAKE, T_cap=16,
+             o=FAKE, B=2, n=4, Hq=8, Hkv=2, d=128, mode=1, window=0, scale=0.0, dt=0, stream=None)
+    a.update(kw)
+    assert lib.hd_sfa_decode_noalloc(*a.values()) == code
+    if kw.get("B") == 1024:
+        assert "scratch" in hd.last_error()
 
 
 def test_workspace_size_is_monotone_and_zero_on_bad_sizes(lib):
@@ -302,7 +318,7 @@ def _decode_args(lens, T_cap=16):
 
 
 @pytest.mark.parametrize("lens", [[3, 16], [-1, 0], [15, 40]])
-@pytest.mark.parametrize("entry", ["hd_sfa_decode"])
+@pytest.mark.parametrize("entry", ["hd_sfa_decode", "hd_sfa_decode_noalloc"])
 def test_debug_mode_rejects_cache_len_outside_the_cache(monkeypatch, lens, entry):
     monkeypatch.setenv("HD_DEBUG", "1")
     with pytest.raises(ValueError, match="T_cap=16"):
@@ -317,7 +333,7 @@ def test_debug_mode_rejects_cache_len_of_final_stream_decode(monkeypatch):
         hd.hd_sfa_decode(qf, kn, vn, kc, vc, cl, torch.empty_like(qf), 1, final_only=True)
 
 
-@pytest.mark.parametrize("entry", ["hd_sfa_decode"])
+@pytest.mark.parametrize("entry", ["hd_sfa_decode", "hd_sfa_decode_noalloc"])
 def test_debug_mode_passes_valid_cache_len_on(monkeypatch, entry):
     monkeypatch.setenv("HD_DEBUG", "1")
     with pytest.raises(TypeError, match="GPU tensor"):
