@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 
 #include "hd.h"
@@ -48,15 +49,25 @@ hd_status device_status(hipError_t e, const char *what) {
         if (_s != HD_OK) return _s;          \
     } while (0)
 
-// Shared validation of the attention sizes.
-hd_status check_attn(int B, int n, int Hq, int Hkv, int d, int mode, int window, hd_dtype dt) {
+// The raw value of an enum a C caller passed (it may lie outside the
+// enumerators, and loading such a value as the enum type is undefined in C++).
+template <typename E>
+int raw_int(const E &e) {
+    static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+    int v;
+    std::memcpy(&v, &e, sizeof v);
+    return v;
+}
+
+// Shared validation of the attention sizes (mode and dtype as raw values).
+hd_status check_attn(int B, int n, int Hq, int Hkv, int d, int mode, int window, int dt) {
     if (B < 1 || n < 1 || Hq < 1 || Hkv < 1)
         return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d n=%d Hq=%d Hkv=%d)", B, n, Hq, Hkv);
     if (n > HD_MAX_STREAMS) return fail(HD_ERR_INVALID, "n=%d above HD_MAX_STREAMS=%d", n, HD_MAX_STREAMS);
     if (Hq % Hkv) return fail(HD_ERR_INVALID, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
     if (window < 0) return fail(HD_ERR_INVALID, "window=%d < 0", window);
     if (d != 32 && d != 64 && d != 128) return fail(HD_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
-    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", dt);
     if (mode != HD_MODE_INTRA && mode != HD_MODE_CROSS) return fail(HD_ERR_UNSUPPORTED, "unknown mode %d", mode);
     return HD_OK;
 }
@@ -99,7 +110,11 @@ hd_status scratch_for_current_device(void **out) {
 extern "C" {
 
 const char *hd_status_string(hd_status s) {
-    switch (s) {
+    // C callers may pass any int: read the raw value (loading an enum outside
+    // its enumerators is undefined in C++)
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
         case HD_OK: return "HD_OK";
         case HD_ERR_INVALID: return "HD_ERR_INVALID";
         case HD_ERR_UNSUPPORTED: return "HD_ERR_UNSUPPORTED";
@@ -117,7 +132,8 @@ hd_status hd_expand_embed(const int32_t *ids, int B, int L, int n, const void *c
     if (B < 1 || L < 1 || n < 1 || V < 1 || D < 1)
         return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d L=%d n=%d V=%lld D=%d)", B, L, n, (long long)V, D);
     if (n > HD_MAX_STREAMS) return fail(HD_ERR_INVALID, "n=%d above HD_MAX_STREAMS=%d", n, HD_MAX_STREAMS);
-    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (raw_int(dt) != HD_BF16 && raw_int(dt) != HD_F32)
+        return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", raw_int(dt));
     if (tables == nullptr) return fail(HD_ERR_INVALID, "tables is NULL");
     HD_TRY(check_ptr(ids, "ids"));
     HD_TRY(check_ptr(out, "out"));
@@ -178,7 +194,7 @@ static void rope_freqs(double *ft, int d, float theta) {
 hd_status hd_sfa_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int B, int L, int n,
                      int Hq, int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt, void *stream) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
-    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, raw_int(mode), window, raw_int(dt)));
     if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
     HD_TRY(check_ptr(q, "q"));
     HD_TRY(check_ptr(k, "k"));
@@ -200,7 +216,7 @@ hd_status hd_sfa_fwd_final(const void *q, const void *k, const void *v, void *o,
                            int Hq, int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt,
                            void *stream) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
-    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, raw_int(mode), window, raw_int(dt)));
     if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
     HD_TRY(check_ptr(q, "q"));
     HD_TRY(check_ptr(k, "k"));
@@ -222,7 +238,7 @@ hd_status hd_sfa_fwd_rope(const void *q, const void *k, const void *v, void *o, 
                           int L, int n, int Hq, int Hkv, int d, hd_mode mode, int window, float scale, float theta,
                           hd_dtype dt, void *stream) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
-    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, raw_int(mode), window, raw_int(dt)));
     if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
     if (!(theta > 0.f) || !std::isfinite(theta)) return fail(HD_ERR_INVALID, "theta=%g must be > 0", (double)theta);
     HD_TRY(check_ptr(q, "q"));
@@ -254,7 +270,8 @@ hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const in
                   int64_t t_mul, int64_t t_add, float theta, hd_dtype dt, void *stream) {
     if (B < 1 || T < 1 || H < 1) return fail(HD_ERR_INVALID, "sizes must be >= 1 (B=%d T=%d H=%d)", B, T, H);
     if (d != 32 && d != 64 && d != 128) return fail(HD_ERR_UNSUPPORTED, "head dim %d not in {32, 64, 128}", d);
-    if (dt != HD_BF16 && dt != HD_F32) return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", (int)dt);
+    if (raw_int(dt) != HD_BF16 && raw_int(dt) != HD_F32)
+        return fail(HD_ERR_UNSUPPORTED, "unknown dtype %d", raw_int(dt));
     if (!(theta > 0.f) || !std::isfinite(theta)) return fail(HD_ERR_INVALID, "theta=%g must be > 0", (double)theta);
     if (pos_mul < 0 || t_mul < 0 || t_add < 0)
         return fail(HD_ERR_INVALID, "pos_mul=%lld, t_mul=%lld, t_add=%lld must be >= 0", (long long)pos_mul,
@@ -274,7 +291,7 @@ hd_status hd_rope(const void *x, void *out, int B, int T, int H, int d, const in
 // this shape (the window does not change it).
 static size_t bwd_ws_bytes(int B, int L, int n, int Hq, int Hkv, int d, hd_dtype dt, bool final_only) {
     if (L < 1 || (int64_t)n * L > (1 << 30)) return 0;
-    if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, dt) != HD_OK) return 0;
+    if (check_attn(B, n, Hq, Hkv, d, HD_MODE_INTRA, 0, raw_int(dt)) != HD_OK) return 0;
     size_t need = 0;
     for (hd_mode mode : {HD_MODE_INTRA, HD_MODE_CROSS}) {
         hd::BwdArgs a{};
@@ -294,7 +311,7 @@ static hd_status sfa_bwd_common(const void *q, const void *k, const void *v, con
                                 int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt, void *workspace,
                                 size_t workspace_bytes, void *stream, bool final_only) {
     if (L < 1) return fail(HD_ERR_INVALID, "L=%d < 1", L);
-    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, raw_int(mode), window, raw_int(dt)));
     if ((int64_t)n * L > (1 << 30)) return fail(HD_ERR_UNSUPPORTED, "n*L=%lld above 2^30", (long long)n * L);
     HD_TRY(check_ptr(q, "q"));
     HD_TRY(check_ptr(k, "k"));
@@ -353,7 +370,7 @@ static hd_status sfa_decode_common(const void *q, const void *k_new, const void 
                                    int Hkv, int d, hd_mode mode, int window, float scale, hd_dtype dt,
                                    void *workspace, size_t workspace_bytes, void *stream, bool final_only,
                                    bool noalloc = false) {
-    HD_TRY(check_attn(B, n, Hq, Hkv, d, (int)mode, window, dt));
+    HD_TRY(check_attn(B, n, Hq, Hkv, d, raw_int(mode), window, raw_int(dt)));
     if (T_cap < 1) return fail(HD_ERR_INVALID, "T_cap=%d < 1", T_cap);
     const int qrows = (final_only ? 1 : n) * (Hq / Hkv);
     if (qrows > 64) return fail(HD_ERR_UNSUPPORTED, "%d query rows per kv head above 64", qrows);

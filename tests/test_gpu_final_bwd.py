@@ -92,6 +92,10 @@ FINAL_BWD_SHAPES = [
     ((1, 1, 1, 2, 1, 64), INTRA, 0),        # one position
     ((1, 300, 4, 4, 2, 128), INTRA, 0),     # g=2; 3 query segments of the dK/dV pass
     ((1, 90, 3, 6, 2, 128), CROSS, 4),      # g=3, window
+    # final-stream cross (non-identity query map) with query segments of the
+    # dK/dV pass and their reduction: 300 final queries over 1200 positions
+    ((1, 300, 4, 8, 2, 128), CROSS, 0),
+    ((1, 300, 4, 8, 2, 128), CROSS, 20),
 ]
 
 
@@ -153,13 +157,17 @@ def test_final_bwd_full_size_sampled(mode):
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
 
 
-def test_final_bwd_deterministic_and_guarded():
-    B, L, n, Hq, Hkv, d = 1, 150, 4, 8, 2, 128
+@pytest.mark.parametrize("L,cases", [
+    (150, ((INTRA, 0), (CROSS, 0), (CROSS, 9))),
+    (300, ((CROSS, 0), (CROSS, 20))),  # query segments on the final-stream cross map: partial rows in the workspace
+])
+def test_final_bwd_deterministic_and_guarded(L, cases):
+    B, n, Hq, Hkv, d = 1, 4, 8, 2, 128
     q, k, v = synth.qkv(B, L, n, Hq, Hkv, d, torch.bfloat16, DEV)
     qf = q[:, n - 1::n].contiguous()
     dof = synth.normal(qf.shape, SEED_DOUT, torch.bfloat16, DEV)
     guard = 4096
-    for mode, window in ((INTRA, 0), (CROSS, 0), (CROSS, 9)):
+    for mode, window in cases:
         o, lse = hd.sfa_fwd_final(qf, k, v, n, mode, window, return_lse=True)
         bufs = [torch.full((x.numel() + 2 * guard,), -7.0, dtype=torch.bfloat16, device=DEV) for x in (qf, k, v)]
         outs = [b_[guard:guard + x.numel()].view(x.shape) for b_, x in zip(bufs, (qf, k, v))]

@@ -259,9 +259,16 @@ def test_decode_vs_oracle(shape, mode, window, dtype):
     np.testing.assert_array_equal(bits(vc), oracle.decode_append(vn.cpu(), vc0, lens).view(bits(vc).dtype))
 
 
-@pytest.mark.parametrize("mode", [INTRA, CROSS])
-@pytest.mark.parametrize("ragged", [False, True])
-def test_decode_full_size_sampled(mode, ragged):
+@pytest.mark.parametrize("mode,window,ragged,nseq", [
+    # the decode workload (64 sequences, 8192 cached tokens): 32 whole
+    # sequences = 4096 query rows against the oracle
+    (INTRA, 0, False, 32), (CROSS, 0, False, 32),
+    # ragged lengths (0 and T_cap-1 included)
+    (INTRA, 0, True, 6), (CROSS, 0, True, 6),
+    # 4096-token sliding window at full size (the window starts mid-split)
+    (INTRA, 4096, False, 8), (CROSS, 4096, False, 8),
+])
+def test_decode_full_size_sampled(mode, window, ragged, nseq):
     cfg = synth.DECODE_8K
     T_cap = cfg.ctx + 8
     if ragged:
@@ -270,19 +277,22 @@ def test_decode_full_size_sampled(mode, ragged):
     else:
         lens = [cfg.ctx] * cfg.B
     q, kn, vn, kc, vc = synth.decode_inputs(cfg.B, cfg.n, cfg.Hq, cfg.Hkv, cfg.d, T_cap, cfg.dtype, DEV)
-    picks = [0, 17, 42, cfg.B - 1]
-    kc0 = [kc[b].cpu() for b in picks]
-    vc0 = [vc[b].cpu() for b in picks]
+    picks = sorted(set([0, cfg.B - 1] + [int(x) for x in np.linspace(0, cfg.B - 1, nseq)]))[:max(nseq, 2)]
+    if ragged:
+        picks = sorted(set(picks[:nseq - 2] + [0, cfg.B - 1]))
+    idx = torch.tensor(picks, device=DEV)
+    # cache rows [0, len) are all the oracle reads; the step writes row len
+    kc0, vc0 = kc[idx].cpu(), vc[idx].cpu()
     cl = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    o = hd.sfa_decode(q, kn, vn, kc, vc, cl, mode, 0)
+    o = hd.sfa_decode(q, kn, vn, kc, vc, cl, mode, window)
     torch.cuda.synchronize()
     assert torch.isfinite(o).all()
-    for j, b in enumerate(picks):
-        want = oracle.sfa_decode(q[b:b + 1].cpu(), kn[b:b + 1].cpu(), vn[b:b + 1].cpu(), kc0[j][None],
-                                 vc0[j][None], [lens[b]], mode, 0)
-        check_bf16(o[b:b + 1], want, f"decode b={b} len={lens[b]} mode={mode}")
-        got_row = bits(kc[b, lens[b]])
-        np.testing.assert_array_equal(got_row, bits(kn[b]))
+    lp = [lens[b] for b in picks]
+    want = oracle.sfa_decode(q[idx].cpu(), kn[idx].cpu(), vn[idx].cpu(), kc0, vc0, lp, mode, window)
+    check_bf16(o[idx], want, f"decode {len(picks)} sequences mode={mode} W={window} ragged={ragged}")
+    for b in picks:
+        np.testing.assert_array_equal(bits(kc[b, lens[b]]), bits(kn[b]))
+        np.testing.assert_array_equal(bits(vc[b, lens[b]]), bits(vn[b]))
 
 
 def test_decode_deterministic_and_guarded():
