@@ -214,22 +214,24 @@ def _cores():
 
 
 def _time_prefill_rows(q, k, v, cfg, budget_s, seed):
-    """Random query rows of a prefill layer through the oracle until the
-    budget is spent; returns (useful flops done, seconds, rows)."""
+    """Distinct random query rows of a prefill layer through the oracle until
+    the budget is spent or every row is done; returns (useful flops done,
+    seconds, rows)."""
     import oracle
 
     nL = cfg.n * cfg.L
     total = cfg.B * nL * cfg.Hq
     rng = np.random.default_rng(seed)
     oracle.sfa_rows(q, k, v, cfg.n, cfg.mode, cfg.window, rows=np.array([0], dtype=np.int64))  # load + warm
+    order = rng.permutation(total).astype(np.int64)  # distinct rows, in random order
     flops, rows_done, batch = 0.0, 0, 32
     t0 = time.perf_counter()
     while rows_done < total:
-        rows = rng.integers(0, total, batch).astype(np.int64)
+        rows = order[rows_done:rows_done + batch]
         oracle.sfa_rows(q, k, v, cfg.n, cfg.mode, cfg.window, rows=rows)
         t = (rows // cfg.Hq) % nL
         flops += float(4 * cfg.d * row_visible_keys(t, cfg.n, cfg.L, cfg.mode, cfg.window).sum())
-        rows_done += batch
+        rows_done += rows.size
         spent = time.perf_counter() - t0
         if spent >= budget_s * 0.95:
             break

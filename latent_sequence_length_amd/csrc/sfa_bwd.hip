@@ -648,6 +648,12 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
     for (int db = 0; db < D / 32; ++db) dq[db] = f32x16{};
 
     const int rsw = swzv(l32);  // swzv(32*kb + l32) == swzv(l32)
+    // Transposed K read jh of 32-dim block db at key rows r0 (a multiple of
+    // 16): within each 16-lane group lane j addresses row r0 + 8jh + 4hi + j/4,
+    // dims 32db + 16g2 + 4(j%4); with the swzv swizzle that is the lane base
+    // below XOR-ed with (db, jh), plus r0*256 (an immediate offset).
+    const unsigned tlane = (unsigned)((4 * hi + (l16 >> 2)) * 256 + ((l16 >> 2) << 6) + (g2 << 5) +
+                                      ((((l16 & 3) >> 1) ^ hi) << 4) + ((l16 & 1) << 3));
     auto tile = [&](const char *cur, int t0) {
         const bool active = (t0 <= lim1) && (p.weff == 0 || t0 + KT - 1 > lim0 - p.weff);
         if (!active) return;
@@ -691,6 +697,8 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
                     dsall[kb * 2 + m2][j] = (bf16)(pr * (dp[kb][r] - Dq));
                 }
         __builtin_amdgcn_sched_barrier(0);
+        unsigned tl = tlane;  // derived per tile, not held across the loop
+        asm volatile("" : "+v"(tl));
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -701,10 +709,8 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
                     s16x4 half[2];
 #pragma unroll
                     for (int jh = 0; jh < 2; ++jh) {
-                        const int row = kb * 32 + 16 * m2 + 8 * jh + 4 * hi + (l16 >> 2);
-                        const int dim = db * 32 + 16 * g2 + 4 * (l16 & 3);
-                        half[jh] = lds_read_tr16(kbuf + row * 256 + (((dim >> 3) ^ swzv(row)) << 4) +
-                                                 ((dim >> 2) & 1) * 8);
+                        const unsigned a = (tl ^ (unsigned)((db << 6) | (jh << 5))) + (kb * 32 + 16 * m2 + 8 * jh) * 256;
+                        half[jh] = lds_read_tr16(kbuf + a);
                     }
                     const s16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
                     dq[db] = mfma32(__builtin_bit_cast(bf16x8, both), dsop, dq[db]);
@@ -759,6 +765,11 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
     __shared__ __attribute__((aligned(4096))) char tb1[RB];
     __shared__ __attribute__((aligned(256))) float sb0[2][DKV_HS][QT];  // lse | D of the rows
     __shared__ __attribute__((aligned(256))) float sb1[2][DKV_HS][QT];
+    // Per-lane constants read back each round (ds_read, counted by lgkmcnt)
+    // instead of being held in registers across the loop: the kernel is at
+    // its register limit, and a spilled value's reload from scratch would wait
+    // (vmcnt counts in order) for the next round's copies issued before it.
+    __shared__ unsigned lane_tab[6][64 * DKV_NW];  // aoff, toff, copy offsets 0..3
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -809,15 +820,14 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
     // 4*(l/16) + i%4, so four per-lane offsets serve all eight instructions
     const int ct = wave / DKV_HS, chh = wave % DKV_HS;
     const int rs = p.qstride * (int)qrs;  // elements between consecutive query rows
-    unsigned voff[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-        voff[m] = (unsigned)((lane >> 4) * rs + (((lane & 15) ^ (4 * (lane >> 4) + m)) * 8)) * 2u;
     auto issue = [&](int k, char *tb, float (*sb)[DKV_HS][QT]) {
         const int h0 = (k / ntq) * DKV_HS, i0 = ibeg + (k % ntq) * QT;
         const int nh = min(DKV_HS, g - h0);
         const int nvalid = min(QT, qend - i0);
         const int64_t qpos0 = q_row(p, b, sub, i0);
+        unsigned voff[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) voff[m] = lane_tab[2 + m][tid];
         if (chh < nh) {
             const bf16 *src = static_cast<const bf16 *>(ct ? p.dout : p.q) + qpos0 * qrs + (int64_t)(kvh * g + h0 + chh) * D;
             char *dst = tb + (ct * DKV_HS + chh) * QTILE;
@@ -857,6 +867,12 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
         const int row = 4 * hi + (l16 >> 2), dim = 16 * g2 + 4 * (l16 & 3);
         toff = (unsigned)(row * 256 + (((dim >> 3) ^ swzv(row)) << 4) + ((dim >> 2) & 1) * 8);
     }
+    lane_tab[0][tid] = aoff;
+    lane_tab[1][tid] = toff;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        lane_tab[2 + m][tid] = (unsigned)((lane >> 4) * rs + (((lane & 15) ^ (4 * (lane >> 4) + m)) * 8)) * 2u;
+    __syncthreads();
     auto round = [&](int k, const char *tb, const float (*sb)[DKV_HS][QT]) {
         const int h0 = (k / ntq) * DKV_HS, i0 = ibeg + (k % ntq) * QT;
         const int nh = min(DKV_HS, g - h0);
@@ -865,8 +881,11 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
         if (!active) return;
         const bool need_mask = (lim_first < jw0 + 31) || (i0 + QT > qend) || (jw0 + 32 > p.Lsub) ||
                                (p.weff != 0 && lim_last - jw0 >= p.weff);
+        const unsigned ao = lane_tab[0][tid], to = lane_tab[1][tid];
+        int hr = hi;  // the lse / D reads' lane part, derived per round (see lane_tab)
+        asm volatile("" : "+v"(hr));
         for (int hh = 0; hh < nh; ++hh) {
-            unsigned qa = lds_addr(tb + hh * QTILE) + aoff, qt = lds_addr(tb + hh * QTILE) + toff;
+            unsigned qa = lds_addr(tb + hh * QTILE) + ao, qt = lds_addr(tb + hh * QTILE) + to;
             asm volatile("" : "+v"(qa), "+v"(qt));  // keep the derived addresses per use
             constexpr unsigned GOFF = DKV_HS * QTILE;  // dO tile of the same head
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -887,13 +906,14 @@ __global__ __launch_bounds__(64 * DKV_NW, 1) void bwd_dkdv_d128_kernel(BwdArgs p
                 for (int jj = 0; jj < 8; ++jj) {
                     const int r = 8 * m2 + jj;
                     const int qi = 16 * m2 + 8 * (jj >> 2) + 4 * hi + (jj & 3);
+                    const int qr = 16 * m2 + 8 * (jj >> 2) + 4 * hr + (jj & 3);  // == qi
                     const int i = i0 + qi, li = i * qmul + qadd;
                     bool vis = true;
                     if (need_mask) vis = kvalid && i < qend && li >= myk && (p.weff == 0 || li - myk < p.weff);
-                    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sb[0][hh][qi] * kLog2e));
+                    const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c2, -sb[0][hh][qr] * kLog2e));
                     const float pr = vis ? e : 0.f;  // a select, not a branch
                     pop[m2][jj] = (bf16)pr;
-                    dsop[m2][jj] = (bf16)(pr * (dp[r] - sb[1][hh][qi]));
+                    dsop[m2][jj] = (bf16)(pr * (dp[r] - sb[1][hh][qr]));
                 }
 #pragma unroll
             for (int m2 = 0; m2 < 2; ++m2)
