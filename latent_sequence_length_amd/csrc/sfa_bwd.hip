@@ -562,7 +562,9 @@ __global__ __launch_bounds__(64 * DQ_NW, 1) void bwd_dq_d128_kernel(BwdArgs p, i
     if (nwg % 8 == 0) {
         const int x = bid % 8, j = bid / 8;
         if (nrest % 8 == 0) {
-            lid = x * (nwg / 8) + j;
+            // the XCD's nrest/8 groups interleaved, longest blocks first
+            const int gpx = nrest / 8;
+            lid = (x * gpx + j % gpx) * nqblk + j / gpx;
         } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
             const int r = 8 / nrest;
             lid = (x / r) * nqblk + j * r + x % r;

@@ -419,8 +419,10 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     // Workgroup -> (query block, group).  Dispatch is round-robin over the 8
     // XCDs (XCD bid % 8 runs its workgroups in bid order); the map keeps each
     // XCD's share balanced (longest blocks first) and its groups few:
-    // whole groups per XCD when the group count is a multiple of 8, each
-    // group spread over 8/G XCDs when G divides 8, else round-robin.
+    // whole groups per XCD when the group count is a multiple of 8 (the
+    // XCD's groups interleaved, so its longest blocks of every group run
+    // first), each group spread over 8/G XCDs when G divides 8, else
+    // round-robin.
     const int nrest = p.B * p.Hkv * ngrp * p.nsub;
     const int nwg = nrest * nqblk;
     const int bid = blockIdx.x;
@@ -428,7 +430,8 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     if (nwg % 8 == 0) {
         const int x = bid % 8, j = bid / 8;
         if (nrest % 8 == 0) {
-            lid = x * (nwg / 8) + j;
+            const int gpx = nrest / 8;
+            lid = (x * gpx + j % gpx) * nqblk + j / gpx;
         } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
             const int r = 8 / nrest;
             lid = (x / r) * nqblk + j * r + x % r;
