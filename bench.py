@@ -8,8 +8,8 @@ are already resident in HBM:
   cross prefill  same shapes as the headline, dense causal over 16384 positions
   decode         64 sequences, 8192 cached tokens x 4 streams, 32 q / 8 kv heads,
                  intra and cross (one new token, 4 stream queries each)
-After the timed steps, the extension rows are timed in a loop of their own
-(reported under "components", outside ms_per_step):
+After the timed steps, the extension rows are timed one row at a time, each
+with its own warm-up calls (reported under "components", outside ms_per_step):
   gather         the same tables at prefill size: B=1, L=4096, n=4 -> 16384 rows
                  (0.47 GB moved; 64 rotating id sets so rows come from HBM)
   long context   n=4, L=32768 (nL=131072), 16 q / 4 kv heads: intra-stream with
@@ -488,7 +488,7 @@ def main():
 
     # The step is one pass over the hot path's rows (gather, prefill n=4 and
     # the n=1 control, cross layer, decode).  With no --only, the extension
-    # rows are timed in a loop of their own after the step, so they neither
+    # rows are timed after the step, one row at a time, so they neither
     # lengthen nor heat the timed step.
     STEP_ROWS = ("intra_n4", "intra_n1", "cross_n4", "decode_intra", "decode_cross", "embed")
     if only:
@@ -518,9 +518,12 @@ def main():
     total_ms = timed_loop(step_comps, args.steps, args.warmup, timer)
     ms_per_step = total_ms / max(args.steps, 1)
     if extra_comps:
-        extra_timer = Timer()
-        timed_loop(extra_comps, args.steps, args.warmup, extra_timer)
-        timer.ms.update(extra_timer.ms)
+        # each extension row on its own, back to back: its calls see only its
+        # own cache state, not the write-back of another row's outputs
+        for name, entry in extra_comps.items():
+            extra_timer = Timer()
+            timed_loop({name: entry}, args.steps, args.warmup, extra_timer)
+            timer.ms.update(extra_timer.ms)
 
     report = {}
     for name, (fn, fl, by) in comps.items():
