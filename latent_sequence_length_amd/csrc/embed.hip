@@ -9,9 +9,9 @@
 //     loads before any store, so a CU with eight such workgroups keeps
 //     ~128 KB of reads in flight; the row, its token id and its table are
 //     wave-uniform (scalar) and only the in-row offset is per lane.  Table
-//     rows are read with non-temporal loads (they are not reused) and the
-//     output rows written with non-temporal stores (the next layer reads them
-//     long after this kernel, so they should not displace L2 lines);
+//     rows are read with non-temporal loads (they are not reused); the
+//     output rows are written with ordinary stores, which measured 11% faster
+//     than non-temporal ones for 16384 rows (0.47 GB moved: 78 vs 88 us);
 //   * shorter rows: one wavefront per row, 16-byte (or 2-byte) lane accesses.
 // An id outside [0, V) breaks the caller's contract; it is clamped to the
 // table so that no read leaves it.
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void expand_embed_rows(EmbedArgs a, int nchunk
 #pragma unroll
     for (int u = 0; u < kPerLane; ++u) {
         const int c = c0 + 256 * u;
-        if (c < nvec) __builtin_nontemporal_store(x[u], dst + c);
+        if (c < nvec) dst[c] = x[u];
     }
 }
 
