@@ -617,6 +617,11 @@ def main():
                    "n": 4, "seq_len_tokens": 4096, "expanded_len": 16384, "batch": 1,
                    "heads_q": 32, "heads_kv": 8, "head_dim": 128},
         "n4_n1_time_ratio": ratio,
+        # the layers' useful-FLOP ratio beside it: a time ratio below it means
+        # the n=1 control runs less efficiently (512 workgroups on 256 CUs),
+        # not that the n=4 layer beats linear cost
+        "n4_n1_flop_ratio": (round(comps["intra_n4"][1] / comps["intra_n1"][1], 3)
+                             if "intra_n4" in comps and "intra_n1" in comps else None),
         # forward + backward of the attention layer (the pages compare training
         # step times); 4.0 would be the FLOP ratio
         "n4_n1_train_time_ratio": (round((report["intra_n4"]["ms"] + report["bwd_intra_n4"]["ms"]) /
