@@ -159,6 +159,26 @@ def test_fwd_bf16_vs_oracle(shape, mode, window):
     check_f32(lse, wlse, "lse", tol=LSE_TOL_BF16)
 
 
+# Layers with more d=128 workgroups than the chip has compute units, each
+# workgroup-to-XCD map branch, compared on every output (the full workloads
+# are only compared on sampled rows).
+MANY_WG_SHAPES = [
+    ((4, 700, 4, 8, 2, 128), INTRA, 0),     # 352 workgroups: whole groups per XCD, ragged tail
+    ((4, 700, 4, 8, 2, 128), INTRA, 100),   # the same with a window
+    ((3, 1984, 1, 12, 3, 128), INTRA, 0),   # 279 workgroups: count not a multiple of 8
+    ((4, 600, 4, 8, 8, 128), CROSS, 0),     # 320 workgroups, MHA (g = 1)
+    ((1, 1024, 4, 16, 4, 128), CROSS, 0),   # 4 groups: each spread over two XCDs
+]
+
+
+@pytest.mark.parametrize("shape,mode,window", MANY_WG_SHAPES)
+def test_fwd_bf16_many_workgroups(shape, mode, window):
+    q, k, v, o, lse = run_fwd(shape, mode, window, torch.bfloat16)
+    want, wlse = oracle.sfa_fwd(q.cpu(), k.cpu(), v.cpu(), shape[2], mode, window)
+    check_bf16(o, want, f"o {shape} mode={mode} W={window}")
+    check_f32(lse, wlse, "lse", tol=LSE_TOL_BF16)
+
+
 def test_fwd_bf16_custom_scale():
     shape = (1, 70, 2, 4, 2, 64)
     q, k, v, o, lse = run_fwd(shape, CROSS, 0, torch.bfloat16, scale=0.05)
