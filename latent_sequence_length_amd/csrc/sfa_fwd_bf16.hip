@@ -28,6 +28,7 @@
 // real k indices to slots is a valid contraction.  The accumulator holds
 // C[8*(r/4) + 4*(l/32) + (r%4)][l % 32] in register r.
 #include "attn_common.h"
+#include "sfa_fwd_d128_loop.inc"
 
 namespace hd {
 
@@ -226,190 +227,51 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //   * a workgroup is 8 waves (HG heads x 8/HG blocks of 32 positions), two
 //     per SIMD and one workgroup per CU, so every K/V tile copied into LDS
 //     serves 256 query rows (half the L2-to-LDS traffic of 4-wave groups);
-//   * each wave raises its issue priority while it issues the QK^T MFMAs, so
-//     the other wave of its SIMD fills the matrix core's gaps with its own
-//     softmax and PV rather than competing for it;
+//   * the key loop is one hand-ordered instruction stream (see
+//     gen_fwd_d128_loop.py): per 32-key sub-tile i, the QK^T MFMAs of i, the
+//     softmax of i-1 and the PV MFMAs of i-2, the softmax's vector ops placed
+//     one by one between the MFMAs so that the vector ALU and the matrix core
+//     of a SIMD work at the same time inside each wave;
 //   * K and V tiles are fetched with direct-to-LDS 16-byte loads
-//     (global_load_lds), double-buffered: tile t+1 is in flight while tile t
-//     is computed, with no VGRPs spent on staging and one barrier per tile;
-//     the tile base is a scalar and each lane's offset is fixed, so issuing a
-//     copy costs no vector ALU work;
-//   * the QK^T MFMAs run as two interleaved accumulator chains with the K
-//     operand reads scheduled eight ahead;
+//     (global_load_lds) into three-deep rings, one barrier per tile: K of
+//     tile t+2 and V of tile t+1 are in flight while tile t is computed, so a
+//     tile's first operand reads can be issued before its barrier; no VGPRs
+//     are spent on staging, and each lane's copy offset is fixed;
 //   * LDS rows are 256 B with the 16-byte chunk index XOR-swizzled by the row
-//     (sw(r) = 2*(r%8) + (r/8)%2), so the K-operand reads (16 rows, one chunk)
-//     and the transposed V reads (8 rows, four chunks) are bank-conflict free;
+//     (K: sw(r) = 2*(r%8) + (r/8)%2, V: 4*(r%4) + (r/4)%4), so the K-operand
+//     reads (16 rows, one chunk) and the transposed V reads are bank-conflict
+//     free; the per-lane LDS addresses are a table of 16 registers, the ring
+//     buffer and row block are immediate offsets;
 //   * the V^T operand comes from two ds_read_b64_tr_b16 per MFMA: within each
 //     16-lane group that instruction returns out[i][e] = in[4e + i/4][i%4],
 //     so lane j of the group addresses key row r0 + j/4, dims d0 + 4*(j%4);
-//   * softmax: the scale is folded into one fma before exp2; a tile's
+//   * softmax: the scale is folded into one fma before exp2; a sub-tile's
 //     probabilities are taken against the running max as it stands and kept
 //     when every lane's share of its row sum stays <= 2^32 (no probability
 //     exceeds 2^32: harmless for fp32 sums and for bf16 P, whose relative
 //     precision does not depend on magnitude); otherwise, and on the first
-//     tile, the wave takes the tile max, rescales O and l and recomputes.
-//     The common tile needs no max, no rescale test and no O rescale; the
-//     final normalisation is unchanged;
+//     sub-tile, the wave takes the tile max, rescales O and l and recomputes.
+//     The row sum l adds the fp32 probabilities (v_add_f32: the packed bf16
+//     dot instruction would stall the matrix core);
+//   * the output goes through LDS so that every store writes 16-byte pieces
+//     of whole rows;
 //   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
 //     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
 constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
 
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSgMfma = 0x008, kSgDsRead = 0x100;
-
-// One tile of the d=128 loop: wait for tile `it` (in buffer `cur`), start
-// the DMA of tile it+1 into `nxt`, then compute tile `it`.  `cur` and `nxt`
-// are distinct __shared__ arrays known at compile time, so the compiler can
-// tell the in-flight DMA and this tile's LDS reads apart.
-struct D128State {
-    f32x16 oacc[4];
-    float m_run, l_run;
-};
-
-template <typename Issue>
-__device__ __forceinline__ void d128_tile(const char *__restrict__ cur, Issue &&issue_next, bool has_next,
-                                          int t0, const FwdArgs &p, int lim0, int lim1, int mylim, int hi, int l32,
-                                          int l16, int g2, const bf16x8 (&qop)[8], float scale_log2,
-                                          D128State &st) {
-    constexpr int D = 128;
-    constexpr int TILE = KT * D * 2;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the tile have landed
-    __syncthreads();                // ... and every wave's; the previous tile is fully consumed
-    if (has_next) issue_next();
-
-    const bool active = (t0 <= lim1) && (p.weff == 0 || t0 + KT - 1 > lim0 - p.weff);
-    if (!active) return;
-    const bool need_mask = (t0 + KT - 1 > lim0) || (t0 + KT > p.Lsub) || (p.weff != 0 && t0 <= lim1 - p.weff);
-    const char *kbuf = cur;
-    const char *vbuf = cur + TILE;
-
-    f32x16 sacc[2];
-    __builtin_amdgcn_s_setprio(1);  // the wave issuing MFMAs wins arbitration on its SIMD
-    // two independent 32-key accumulator chains, interleaved; the K-operand
-    // reads are scheduled eight ahead of the MFMAs that consume them
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sacc[kb] = f32x16{};
-    const int ksw = swz128(l32) ^ hi;  // swz128(32*kb + l32) == swz128(l32); 2*ks + hi == (2*ks) ^ hi
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kbuf + (kb * 32 + l32) * 256 + (((2 * ks) ^ ksw) << 4));
-            sacc[kb] = mfma32(a, qop[ks], sacc[kb]);
-        }
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-
-    __builtin_amdgcn_s_setprio(0);
-    if (need_mask) {
-        // visible <=> lo <= key <= hi, checked as one unsigned compare
-        const int lo = p.weff ? mylim - p.weff + 1 : 0;
-        const int hi_key = min(mylim, p.Lsub - 1);
-        const unsigned span = (unsigned)(hi_key - lo);
-        const int base = t0 + 4 * hi - lo;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const unsigned u = (unsigned)(base + kb * 32 + 8 * (r >> 2) + (r & 3));
-                sacc[kb][r] = (u <= span) ? sacc[kb][r] : -INFINITY;
-            }
-    }
-    // Probabilities against the running max; the tile is accepted as is when
-    // every lane's share of its row sum stays <= 2^32 (so no probability
-    // exceeds it), else -- and while some row has no max yet -- the wave
-    // raises every row's max to the tile's, rescales and recomputes.
-    bf16x8 pop[4];
-    float lsum = 0.f;
-    auto probs = [&](float neg_m) {
-        lsum = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int m2 = 0; m2 < 2; ++m2) {
-                bf16x8 pp;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    pp[j] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * m2 + j], scale_log2, neg_m));
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 0, 1), kOnes2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 2, 3), kOnes2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 4, 5), kOnes2, lsum, false);
-                lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pp, pp, 6, 7), kOnes2, lsum, false);
-                pop[kb * 2 + m2] = pp;
-            }
-    };
-    bool slow = true;
-    if (!__ballot(st.m_run == -INFINITY)) {
-        probs(-st.m_run);
-        slow = __ballot(!(lsum <= 4294967296.f)) != 0;  // also catches inf / NaN
-    }
-    if (slow) {
-        float m0 = fmaxf(sacc[0][0], sacc[0][1]), m1 = fmaxf(sacc[1][0], sacc[1][1]);
-#pragma unroll
-        for (int r = 2; r < 16; r += 2) {
-            m0 = fmaxf(m0, fmaxf(sacc[0][r], sacc[0][r + 1]));
-            m1 = fmaxf(m1, fmaxf(sacc[1][r], sacc[1][r + 1]));
-        }
-        const float m_tile = pair_max(fmaxf(m0, m1)) * scale_log2;
-        const float m_new = fmaxf(st.m_run, m_tile);
-        const float alpha = (m_new == st.m_run) ? 1.f : __builtin_amdgcn_exp2f(st.m_run - m_new);
-        if (__ballot(alpha != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) st.oacc[db] *= alpha;
-        }
-        st.l_run *= alpha;
-        st.m_run = m_new;
-        probs((m_new == -INFINITY) ? 0.f : -m_new);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int m2 = 0; m2 < 2; ++m2) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                s16x4 half[2];
-#pragma unroll
-                for (int jh = 0; jh < 2; ++jh) {
-                    const int row = kb * 32 + 16 * m2 + 8 * jh + 4 * hi + (l16 >> 2);
-                    const int dim = db * 32 + 16 * g2 + 4 * (l16 & 3);
-                    const char *addr = vbuf + row * 256 + (((dim >> 3) ^ swzv(row)) << 4) + ((dim >> 2) & 1) * 8;
-                    half[jh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4 *)(addr));
-                }
-                const s16x8 both = __builtin_shufflevector(half[0], half[1], 0, 1, 2, 3, 4, 5, 6, 7);
-                st.oacc[db] = mfma32(__builtin_bit_cast(bf16x8, both), pop[kb * 2 + m2], st.oacc[db]);
-            }
-        }
-    // the 32 transposed V reads run eight ahead of the 16 PV MFMAs, two per
-    // MFMA after that (measured best of 4..16 ahead: -2% on every layer)
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 4, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    st.l_run += lsum;
-}
-
 // GQ: the query map is not the identity (qmul, qadd) != (1, 0); a full layer
-// runs the GQ = false instance, whose band tests are the plain p <= j ones.
+// runs the GQ = false instance (compile-time identity map).
 // ROPE: q is rotated at its expanded position right after the load.
+// This function does the work-item map, loads Q, builds the per-lane LDS
+// address tables and copy offsets the key loop (sfa_fwd_d128_loop.inc) uses,
+// binds them to the registers the loop expects, and writes the output.
 template <bool GQ, bool ROPE>
 __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
                                                                   float scale_log2) {
     constexpr int D = 128;
     constexpr int TILE = KT * D * 2;  // 16 KB per K or V tile
-    __shared__ __attribute__((aligned(1024))) char buf0[2 * TILE];  // K | V, even tiles
-    __shared__ __attribute__((aligned(1024))) char buf1[2 * TILE];  // K | V, odd tiles
+    __shared__ __attribute__((aligned(1024))) char lds[6 * TILE];  // K ring (3 tiles) | V ring (3 tiles)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -460,60 +322,80 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const int64_t krs = (int64_t)p.Hkv * D;
     const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;              // key element 0
     const int64_t qbase = (int64_t)b * p.qrows + (int64_t)sub * p.qsub;  // query 0's Q row
-    const bf16 *qg = static_cast<const bf16 *>(p.q);
-    const bf16 *kg = static_cast<const bf16 *>(p.k) + (int64_t)kvh * D;
-    const bf16 *vg = static_cast<const bf16 *>(p.v) + (int64_t)kvh * D;
 
     const int kend = min((min(q0 + QB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
     const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
     const int tfirst = kbeg & ~(KT - 1);
     const int ntiles = (kend - tfirst + KT - 1) / KT;
 
-    // Each wave moves 4 x 1 KB of K and of V per tile: slots w*256 .. +255,
-    // slot s = row*16 + physical chunk; lane l of instruction i fills slot
-    // (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).  Rows past the end
-    // of the sub-sequence re-read its last row (finite data, masked later).
+    // LDS address tables.  K operand of k-step ks (keys 0-31 of ring buffer
+    // 0): row l32, 16-byte chunk (2ks + hi) ^ sw(row).  V^T half-operand
+    // (db, jh) (keys 0-15 of V buffer 0): ds_read_b64_tr_b16 lane j of a
+    // 16-lane group addresses key 8jh + 4hi + j/4, dims 32db + 16g2 + 4(j%4);
+    // with the V swizzle 4*(r%4) + (r/4)%4 the chunk index splits into
+    // 4*(db ^ r4) + ((2g2 + c1) ^ (2jh + hi)).  The loop adds ring buffer,
+    // 32-key half and 16-key row block as immediate offsets.
+    const unsigned ldsk = lds_addr(lds), ldsv = ldsk + 3 * TILE;
+    unsigned kaddr[8], vaddr[8];
+    {
+        const int ksw = swz128(l32) ^ hi;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kaddr[ks] = ldsk + l32 * 256 + (((2 * ks) ^ ksw) << 4);
+        const int r4 = l16 >> 2, c1 = (l16 & 3) >> 1, c0 = l16 & 1;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh)
+                vaddr[db * 2 + jh] = ldsv + (8 * jh + 4 * hi + r4) * 256 +
+                                     16 * (4 * (db ^ r4) + ((2 * g2 + c1) ^ (2 * jh + hi))) + 8 * c0;
+    }
+
+    // Copies: each wave moves 2 x 1 KB of K and of V per tile: slots
+    // w*128 .. +127, slot s = row*16 + physical chunk; lane l of copy i fills
+    // slot (w*2+i)*64 + l with logical chunk (s%16) ^ sw(row).  A tile with
+    // rows past the end of the sub-sequence re-reads its last row there
+    // (finite data, masked in the loop).
     const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
-    constexpr int PER = 16 / D128_NW;  // 1 KB copies of K (and of V) per wave per tile
-    int lrow[PER], lchunk[PER], lchunkv[PER];
+    unsigned boff[2], boffv[2], toff[2], toffv[2];
+    const int tlast = tfirst + (ntiles - 1) * KT;
+    const int rmax = p.Lsub - 1 - tlast;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        lrow[i] = (wave * PER + i) * 4 + (lane >> 4);
-        lchunk[i] = ((lane & 15) ^ swz128(lrow[i])) * 8;
-        lchunkv[i] = ((lane & 15) ^ swzv(lrow[i])) * 8;
+    for (int i = 0; i < 2; ++i) {
+        const int lrow = (wave * 2 + i) * 4 + (lane >> 4);
+        const int lc = ((lane & 15) ^ swz128(lrow)) * 8, lcv = ((lane & 15) ^ swzv(lrow)) * 8;
+        boff[i] = (unsigned)(lrow * rstride + lc) * 2u;
+        boffv[i] = (unsigned)(lrow * rstride + lcv) * 2u;
+        toff[i] = (unsigned)(min(lrow, rmax) * rstride + lc) * 2u;
+        toffv[i] = (unsigned)(min(lrow, rmax) * rstride + lcv) * 2u;
     }
-    unsigned boff[PER], boffv[PER];  // per-lane byte offsets of K / V within a tile (rows unclamped)
+    const int tailt = rmax < KT - 1 ? ntiles - 1 : -1;
+    const int64_t tile0 = (bpos + (int64_t)tfirst * p.stride) * krs + (int64_t)kvh * D;  // elements
+    const void *kptr = static_cast<const bf16 *>(p.k) + tile0;
+    const void *vptr = static_cast<const bf16 *>(p.v) + tile0;
+    const unsigned tbytes = (unsigned)(KT * rstride) * 2u;
+    const unsigned ldsw = ldsk + (unsigned)wave * 2048u;  // this wave's copy slots in a ring buffer
+
+    // Copies of K(0), K(1) and V(0), in flight while Q is loaded; the loop
+    // copies K(T+2) and V(T+1) at the start of tile T.
+    if (ntiles > 0) {
+        const char *k0 = static_cast<const char *>(kptr), *v0 = static_cast<const char *>(vptr);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        boff[i] = (unsigned)(lrow[i] * rstride + lchunk[i]) * 2u;
-        boffv[i] = (unsigned)(lrow[i] * rstride + lchunkv[i]) * 2u;
-    }
-    auto issue = [&](int t0, char *dst) {
-        const int64_t tbase = (bpos + (int64_t)t0 * p.stride) * krs;
-        const bf16 *kt = kg + tbase, *vt = vg + tbase;
-        const int rmax = p.Lsub - 1 - t0;
-        unsigned bo[PER], bv[PER];
+        for (int i = 0; i < 2; ++i) lds_dma16_s(k0, tailt == 0 ? toff[i] : boff[i], ldsw + i * 1024);
+        if (ntiles > 1) {
 #pragma unroll
-        for (int i = 0; i < PER; ++i) { bo[i] = boff[i]; bv[i] = boffv[i]; }
-        if (rmax < KT - 1) {  // tail tile: rows past the end re-read the last row
-#pragma unroll
-            for (int i = 0; i < PER; ++i) {
-                bo[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunk[i]) * 2u;
-                bv[i] = (unsigned)(min(lrow[i], rmax) * rstride + lchunkv[i]) * 2u;
-            }
+            for (int i = 0; i < 2; ++i)
+                lds_dma16_s(k0 + tbytes, tailt == 1 ? toff[i] : boff[i], ldsw + TILE + i * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int s0 = (wave * PER + i) * 64;
-            lds_dma16_s(kt, bo[i], lds_addr(dst + s0 * 16));
-            lds_dma16_s(vt, bv[i], lds_addr(dst + TILE + s0 * 16));
-        }
-    };
-    if (ntiles > 0) issue(tfirst, buf0);
+        for (int i = 0; i < 2; ++i) lds_dma16_s(v0, tailt == 0 ? toffv[i] : boffv[i], ldsw + 3 * TILE + i * 1024);
+    }
+    const void *kptr2 = static_cast<const char *>(kptr) + 2 * (size_t)tbytes;
+    const void *vptr1 = static_cast<const char *>(vptr) + tbytes;
 
     bf16x8 qop[D / 16];
     {
-        const bf16 *qp = qg + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs + (int64_t)h * D;
+        const bf16 *qp = static_cast<const bf16 *>(p.q) + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs +
+                         (int64_t)h * D;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
@@ -523,38 +405,71 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
         if (ROPE) rope_rotate_q<D>(qop, p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
     }
 
-    D128State st;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) st.oacc[db] = f32x16{};
-    st.m_run = -INFINITY;
-    st.l_run = 0.f;
 
-    for (int it = 0; it < ntiles; it += 2) {
-        const int t0 = tfirst + it * KT;
-        d128_tile(buf0, [&] { issue(t0 + KT, buf1); }, it + 1 < ntiles, t0, p, lim0, lim1, mylim, hi, l32, l16, g2,
-                  qop, scale_log2, st);
-        if (it + 1 < ntiles)
-            d128_tile(buf1, [&] { issue(t0 + 2 * KT, buf0); }, it + 2 < ntiles, t0 + KT, p, lim0, lim1, mylim, hi,
-                      l32, l16, g2, qop, scale_log2, st);
+    // Band of this lane (key k visible <=> k - lo <= span, unsigned) and the
+    // wave's 32-key sub-tiles that need the mask: j < jw (window start) or
+    // j >= jm (the diagonal or the end of the sub-sequence).
+    const int lo = p.weff ? mylim - p.weff + 1 : 0;
+    const int span = min(mylim, p.Lsub - 1) - lo;
+    const int maskbase = 4 * hi - lo;
+    const int mfull = min(lim0, p.Lsub - 1) - 31 - tfirst;
+    const int jm = mfull >= 0 ? mfull / 32 + 1 : 0;
+    const int wfull = lim1 - p.weff - tfirst;
+    const int jw = (p.weff && wfull >= 0) ? wfull / 32 + 1 : 0;
+    f32x16 o0 = {}, o1 = {}, o2 = {}, o3 = {};
+    float m_run = -INFINITY, l_run = 0.f;
+    if (ntiles > 0) {
+        asm volatile(HD_FWD_D128_LOOP
+                     : "+{v[0:15]}"(o0), "+{v[16:31]}"(o1), "+{v[32:47]}"(o2), "+{v[48:63]}"(o3), "+{v96}"(m_run),
+                       "+{v97}"(l_run)
+                     : "{v[64:67]}"(qop[0]), "{v[68:71]}"(qop[1]), "{v[72:75]}"(qop[2]), "{v[76:79]}"(qop[3]),
+                       "{v[80:83]}"(qop[4]), "{v[84:87]}"(qop[5]), "{v[88:91]}"(qop[6]), "{v[92:95]}"(qop[7]),
+                       "{v98}"(maskbase), "{v99}"(span), "{v100}"(kaddr[0]), "{v101}"(kaddr[1]),
+                       "{v102}"(kaddr[2]), "{v103}"(kaddr[3]), "{v104}"(kaddr[4]), "{v105}"(kaddr[5]),
+                       "{v106}"(kaddr[6]), "{v107}"(kaddr[7]), "{v108}"(vaddr[0]), "{v109}"(vaddr[1]),
+                       "{v110}"(vaddr[2]), "{v111}"(vaddr[3]), "{v112}"(vaddr[4]), "{v113}"(vaddr[5]),
+                       "{v114}"(vaddr[6]), "{v115}"(vaddr[7]), "{v116}"(boff[0]), "{v117}"(boff[1]),
+                       "{v118}"(boffv[0]), "{v119}"(boffv[1]), "{v120}"(toff[0]), "{v121}"(toff[1]),
+                       "{v122}"(toffv[0]), "{v123}"(toffv[1]), [nt] "s"(ntiles), [kt0] "s"(tfirst),
+                       [kptr2] "s"(kptr2), [vptr1] "s"(vptr1), [tbytes] "s"(tbytes), [tailt] "s"(tailt), [jw] "s"(jw),
+                       [jm] "s"(jm), [sc] "s"(scale_log2), [ldsw] "s"(ldsw)
+                     : HD_FWD_D128_CLOBBERS);
     }
 
-    const float l_tot = pair_sum(st.l_run);
-    if (qvalid) {
-        const float inv = 1.f / l_tot;
-        const int64_t qrow = qbase + (int64_t)myq * p.qstride;
-        bf16 *op = static_cast<bf16 *>(p.o) + qrow * qrs + (int64_t)h * D;
+    const float l_tot = pair_sum(l_run);
+    const float inv = 1.f / l_tot;
+    // The wave's 32 output rows go through LDS (free once every wave has left
+    // the loop), so that each store writes 16-byte pieces of whole 256-byte
+    // rows (16 lanes per row) instead of 8 bytes in each of 32 rows.
+    __syncthreads();
+    constexpr int OPITCH = 272;  // bytes per staged row (16-byte aligned, spreads the banks)
+    char *ost = lds + wave * QW * OPITCH;
+    {
+        const f32x16 oacc[4] = {o0, o1, o2, o3};
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 bf16x4 y;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (bf16)(st.oacc[db][4 * r4 + e] * inv);
-                *reinterpret_cast<bf16x4 *>(op + db * 32 + 8 * r4 + 4 * hi) = y;
+                for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[db][4 * r4 + e] * inv);
+                *reinterpret_cast<bf16x4 *>(ost + l32 * OPITCH + (db * 32 + 8 * r4 + 4 * hi) * 2) = y;
             }
-        if (p.lse != nullptr && hi == 0)
-            p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] =
-                st.m_run * kLn2 + __logf(l_tot);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staged rows are in LDS
+#pragma unroll
+    for (int i = 0; i < QW / 4; ++i) {
+        const int row = 4 * i + (lane >> 4), c = lane & 15;
+        const uint4 x = *reinterpret_cast<const uint4 *>(ost + row * OPITCH + c * 16);
+        const int q = qw0 + row;
+        if (q < p.Lq) {
+            const int64_t qrow = qbase + (int64_t)q * p.qstride;
+            *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(p.o) + (qrow * qrs + (int64_t)h * D) * 2 + c * 16) = x;
+        }
+    }
+    if (qvalid && p.lse != nullptr && hi == 0) {
+        const int64_t qrow = qbase + (int64_t)myq * p.qstride;
+        p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] = m_run * kLn2 + __logf(l_tot);
     }
 }
 
