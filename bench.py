@@ -150,7 +150,7 @@ def measured_traffic(name):
     """HBM bytes per launch of a kernel from its committed PMC summary
     (profiles/<name>.md: FETCH_SIZE + WRITE_SIZE scaled by a copy kernel), or
     None when the summary is missing or the kernel source has changed since
-    the counters were taken (the summary records the source's SHA-256)."""
+    the counters were taken (the summary records the sources' SHA-256)."""
     path = os.path.join(ROOT, "profiles", name + ".md")
     if not os.path.exists(path):
         return None
@@ -162,7 +162,12 @@ def measured_traffic(name):
     src = fields.get("source")
     if not src or "traffic_bytes_per_launch" not in fields:
         return None
-    digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    # `source` may list several files (a kernel and the code it includes),
+    # comma-separated; the digest is taken over their bytes in that order.
+    h = hashlib.sha256()
+    for part in src.split(","):
+        h.update(open(os.path.join(ROOT, part.strip()), "rb").read())
+    digest = h.hexdigest()
     if digest != fields.get("source_sha256"):
         return None
     return int(fields["traffic_bytes_per_launch"])
