@@ -97,7 +97,9 @@ def row_visible_keys(t, n, L, mode, window):
 def measured_peaks(dev):
     """The machine's sustained rates, reported beside the published peaks:
     an MFMA-only loop (8 independent bf16 32x32x16 chains per wave, 4 waves
-    per SIMD), a read-only stream over 8 GiB (16-byte non-temporal loads; the
+    per SIMD) on constant operands and on random operands that change from
+    one MFMA to the next (the chip's clock, and so the rate, depends on the
+    operands' switching activity), a read-only stream over 8 GiB (16-byte non-temporal loads; the
     HBM ceiling of a read-dominated kernel such as decode) and, for context,
     a 1 GiB device copy (read + write, torch)."""
     out = {}
@@ -119,6 +121,23 @@ def measured_peaks(dev):
         torch.cuda.synchronize()
         if fl > 0:
             out["mfma_bf16_TFLOPs"] = round(fl / s.elapsed_time(e) / 1e9, 1)
+        if hasattr(lib, "hd_probe_mfma_bf16_random"):
+            lib.hd_probe_mfma_bf16_random.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                                                      ctypes.c_void_p, ctypes.c_void_p]
+            lib.hd_probe_mfma_bf16_random.restype = ctypes.c_double
+            g = torch.Generator(device=dev)
+            g.manual_seed(7)
+            nops = 1 << 20
+            ops = torch.randn(nops, 8, generator=g, device=dev).to(torch.bfloat16)
+            rargs = (blocks, iters // 8, ctypes.c_void_p(ops.data_ptr()), nops, ctypes.c_void_p(sink.data_ptr()), st)
+            lib.hd_probe_mfma_bf16_random(*rargs)
+            s.record()
+            fl = sum(lib.hd_probe_mfma_bf16_random(*rargs) for _ in range(5))
+            e.record()
+            torch.cuda.synchronize()
+            if fl > 0:
+                out["mfma_bf16_random_TFLOPs"] = round(fl / s.elapsed_time(e) / 1e9, 1)
+            del ops
         del sink
         nbytes = 8 << 30
         buf = torch.full((nbytes,), 0x5A, dtype=torch.uint8, device=dev)
@@ -556,7 +575,9 @@ def main():
                 "traffic": measured_traffic("sfa_fwd_bf16_d128__intra_n4_L4096__hbm_bytes"),
                 "kernel": "sfa_fwd_bf16_d128_kernel", "per_launch_flops": fl,
                 "peak_measured": peaks.get("mfma_bf16_TFLOPs") if peaks else None,
-                "frac_measured": frac_measured(ach, "mfma_bf16_TFLOPs")}
+                "frac_measured": frac_measured(ach, "mfma_bf16_TFLOPs"),
+                "peak_measured_random": peaks.get("mfma_bf16_random_TFLOPs") if peaks else None,
+                "frac_measured_random": frac_measured(ach, "mfma_bf16_random_TFLOPs")}
 
     def hbm_roof(name, kernels, traffic_profile):
         if name not in report:

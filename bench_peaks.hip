@@ -6,7 +6,14 @@
 //                       v_mfma_f32_32x32x16_bf16 accumulator chains on
 //                       register operands: no memory traffic and no LDS, so
 //                       its rate is the sustained bf16 matrix-core rate at the
-//                       clock the chip holds under that load.
+//                       clock the chip holds under that load.  The operands
+//                       are small constants, the lowest-power case.
+//   hd_probe_mfma_bf16_random  the same chains on random bf16 operands that
+//                       change from one MFMA to the next (8 A and 8 B
+//                       fragments per lane, loaded once, B rotating over the
+//                       chains): the matrix-core rate with the switching
+//                       activity of real data, at the clock the chip holds
+//                       under that power.
 //   hd_probe_hbm_read   a read-only stream over a large buffer: 16-byte
 //                       non-temporal loads, eight in flight per lane, folded
 //                       into one register (XOR) per lane; nothing is written
@@ -43,6 +50,32 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float *sink) 
     if (s == -1.f) sink[blockIdx.x * 256 + threadIdx.x] = s;  // never true; keeps the work alive
 }
 
+__global__ __launch_bounds__(256) void mfma_random_kernel(int rounds, const bf16x8_t *ops, int64_t nops,
+                                                          float *sink) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    bf16x8_t a[8], b[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        a[c] = ops[(gid * 16 + c) % nops];
+        b[c] = ops[(gid * 16 + 8 + c) % nops];
+    }
+    f32x16_t acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x16_t{};
+    for (int i = 0; i < rounds; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[(c + j) & 7], acc[c], 0, 0, 0);
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[c][r];
+    if (s == -1.f) sink[blockIdx.x * 256 + threadIdx.x] = s;  // (almost) never true; keeps the work alive
+}
+
 constexpr int kReadUnroll = 8;
 
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4_t *src, int64_t nvec, unsigned *sink) {
@@ -71,6 +104,20 @@ double hd_probe_mfma_bf16(int blocks, int iters, float *sink, void *stream) {
     hipLaunchKernelGGL(mfma_peak_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
     if (hipGetLastError() != hipSuccess) return -1.0;
     return (double)blocks * 4 * iters * 8 * (2.0 * 32 * 32 * 16);
+}
+
+// Random-operand variant: `rounds` rounds of 64 MFMAs per wave on operands
+// taken from the nops bf16x8 fragments at `ops` (device memory); returns the
+// FLOP count or -1 on a bad argument or launch error.
+double hd_probe_mfma_bf16_random(int blocks, int rounds, const void *ops, int64_t nops, float *sink,
+                                 void *stream) {
+    if (blocks < 1 || rounds < 1 || ops == nullptr || nops < 16 || sink == nullptr ||
+        (reinterpret_cast<uintptr_t>(ops) & 15))
+        return -1.0;
+    hipLaunchKernelGGL(mfma_random_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), rounds,
+                       static_cast<const bf16x8_t *>(ops), nops, sink);
+    if (hipGetLastError() != hipSuccess) return -1.0;
+    return (double)blocks * 4 * rounds * 64 * (2.0 * 32 * 32 * 16);
 }
 
 // Read nbytes (a multiple of 16) from the 16-byte aligned device buffer src

@@ -1,127 +1,164 @@
 """Writes sfa_fwd_d128_loop.inc: the key-tile loop of the head-dim-128 prefill
-kernel as one hand-scheduled gfx950 instruction stream.
+kernel as one hand-scheduled gfx950 instruction stream, for a wave of 64
+queries (two 32-query halves) at one wave per SIMD.
 
-The loop is software-pipelined over 32-key sub-tiles i = 0, 1, ...:
-iteration i runs the QK^T MFMAs of sub-tile i, the softmax of sub-tile i-1
-(vector ALU) and the PV MFMAs of sub-tile i-2, with the softmax instructions
-placed one by one between the MFMAs (a cost-aware list schedule, each op at
+The loop is software-pipelined over 32-key sub-tiles i = 0, 1, ...: iteration
+i issues the QK^T MFMAs of sub-tile i (8 k-steps x 2 halves; each K fragment
+read from LDS feeds both halves), the softmax of sub-tile i-1 (vector ALU, both
+halves) and the PV MFMAs of sub-tile i-2 (2 key steps x 4 dim blocks x 2
+halves; each V^T fragment feeds both halves).  The softmax instructions are
+placed one by one between the MFMAs by a cost-aware list schedule (each op at
 least one MFMA after its inputs), so that the vector ALU and the matrix core
-of a SIMD work at the same time within one wave.  Operands are read from LDS
-two MFMAs ahead into small register rings.  64-key K and V tiles are copied
-direct to LDS into three-deep rings (K of tile T+2 and V of tile T+1 are
-copied while tile T is computed), one barrier per tile, so the first operand
-reads of the next tile can be issued before its barrier.
+work at the same time within the wave; operands are read from LDS two reads
+ahead into small register rings.  64-key K and V tiles are copied direct to
+LDS into three-deep rings with one barrier per tile: K of tile T+2 and V of
+tile T+1 are copied during tile T, from the first MFMA slots of the tile, and
+the tile header waits only for the K copies (V is first read two tiles after
+its copy starts), so the next tile's first operand reads can be issued before
+its barrier.
 
 The softmax uses only instructions that issue beside the MFMAs: v_fma_f32,
 v_exp_f32, v_cvt_pk_bf16_f32 and v_add_f32 (the row sum adds the fp32
 probabilities; the packed bf16 dot instruction stalls the matrix core).  A
 sub-tile's probabilities are taken against the running maximum as it stands;
 when some row has no maximum yet or a lane's share of its row sum exceeds
-2^32, an out-of-line path takes the tile maximum, rescales O and l and
-recomputes them.  Band masks (diagonal, sequence end, window start) are
-applied to a sub-tile's scores before its softmax, on the sub-tiles that
-need them only.  Every hazard the hardware does not check is padded here:
-MFMA results are read by vector ops at least eight MFMAs later (or after
-s_nop), a transcendental result is not read by the next instruction, VCC
-written by a compare is read after s_nop 4.
+2^32, an out-of-line path takes the sub-tile maximum of both halves, rescales
+O and l and recomputes the probabilities.  Band masks (diagonal, sequence
+end, window start) are applied to a sub-tile's scores before its softmax, on
+the sub-tiles that need them only.  After the loop the block sums l over the
+lane pair, scales O by 1/l (hardware reciprocal and one Newton step) and
+writes the bf16 rows to LDS, where the caller picks them up for whole-row
+stores.  Every hazard the hardware does not check is padded here: MFMA
+results are read by vector ops at least eight MFMAs later (or after s_nop),
+a transcendental result is not read by the next instruction, a compare's
+mask is read after s_nop 1.
 
 Run `python gen_fwd_d128_loop.py` after editing; the output is committed.
 Register map (per lane):
-  v[0:63]    O^T accumulators, dims 32*db .. +31 in v[16db : 16db+15]
-  v[64:95]   Q^T operand of k-step ks in v[64+4ks : 67+4ks]
-  v96, v97   running max (log2 units) and row sum of this lane's query
-  v98, v99   mask: 4*hi - lo and span (key k visible <=> k - lo <= span, unsigned)
-  v[100:107] LDS byte address of the K operand of k-step ks (K ring buffer 0, keys 0-31)
-  v[108:115] LDS byte address of the V^T half-operand (db, jh) (V ring buffer 0, keys 0-15)
-  v[116:119] copy offsets of this lane: K slot 0, K slot 1, V slot 0, V slot 1
-  v[120:123] the same for a tile with rows past the end of the sub-sequence
-  v[128:159] score accumulators of two sub-tiles (S^T blocks): lane l holds
-             query l % 32, register r key 8(r/4) + 4(l/32) + r%4 of the sub-tile
-  v[160:175] bf16 probabilities of two sub-tiles
-  v[176:191] K operand ring, v[192:207] V^T operand ring
-  v[208:213], v[214:219] fma and exp result rings
-  v220 row sum of the sub-tile, v221 -max (0 while no max), v222..v224 temps,
-  v225, v226 partial row sums, v229 -inf, v230 2^32
-Scalar registers s80..s93 are the loop's; the caller passes the rest as operands.
+  a[0:127]   O^T accumulators of half h, dims 32db..+31: a[64h+16db : +15]
+             (MFMA accumulators in AGPRs cost nothing; A / B operands read
+             from AGPRs slow the loop down, so Q stays in VGPRs)
+  v[0:63]    score accumulators: sub-tile buffer u, half h: v[32u+16h : +15]
+  v[64:95]   bf16 probabilities: buffer u, half h: v[64+16u+8h : +7]
+  v[96:159]  Q^T operand of half h, k-step ks: v[96+32h+4ks : +3]
+  v160, v161 running max of half 0 / 1 (log2 units); v162, v163 row sums
+  v[164:171] LDS byte address of the K operand of k-step ks (K buffer 0, keys 0-31)
+  v[172:179] LDS byte address of the V^T half-operand (db, jh) (V buffer 0, keys 0-15)
+  v[180:183] K copy offsets, v[184:187] V copy offsets (4 per tile per wave)
+  v[188:195] the same for a tile with rows past the end of the sub-sequence
+  v196, v197 mask base (4*hi - lo) of half 0 / 1; v198, v199 span
+  v[200:211] K operand ring, v[212:223] V^T operand ring
+  v[224:229] fma ring, v[230:235] exp ring
+  v236, v237 sub-tile row sums (1/l after the loop); v[238:241] partial row
+             sums; v242, v243 -max; v[244:246] temporaries; v247 -inf;
+             v248 2^32; v249 staging address
+Scalar registers s80..s93 are the loop's.
 """
 import os
+import sys
 
-KT_BYTES = 16384          # one 64-key tile of K or V in LDS
-V_RING = 3 * KT_BYTES     # V ring starts after the K ring
-LOOK = 2                  # LDS operand reads run this many MFMAs ahead
-RING = 4                  # operand ring entries
+KT_BYTES = 16384
+V_RING = 3 * KT_BYTES
+LOOK = 4                  # MFMA slots ahead that operand reads are issued (2 reads)
+RING = 3                  # operand ring entries (enough for two reads ahead)
 COST = {"fma": 5, "exp": 12, "cvt": 5}  # vector cycles of one wave64 op (measured)
-BUDGET = 26               # vector-ALU cycles placed after one MFMA
+BUDGET = 30               # vector-ALU cycles placed after one MFMA
+CMPNOP = "s_nop 1"        # wait states between a compare and the reader of its mask
 
-S_BASE = (128, 144)
-P_BASE = (160, 168)
-F_RING, E_RING = 208, 214
+S_AT = lambda u, h: 32 * u + 16 * h
+P_AT = lambda u, h: 64 + 16 * u + 8 * h
+Q_V = lambda h, ks: 96 + 32 * h + 4 * ks          # Q^T operands in VGPRs (an AGPR B operand is slow)
+M = (160, 161)
+L = (162, 163)
+KADDR, VADDR = 164, 172
+CPK, CPV, TPK, TPV = 180, 184, 188, 192
+MB, SPAN = (196, 197), (198, 199)
+KRING = 200
+VRING = KRING + 4 * RING
+F_RING = VRING + 4 * RING
+NRING = 6
+E_RING = F_RING + NRING
+RS = (E_RING + NRING, E_RING + NRING + 1)
+PART = RS[1] + 1
+NM = (PART + 4, PART + 5)
+T = PART + 6
+NINF, TWO32 = T + 3, T + 4
+STG = TWO32 + 1
+LAST = STG
+assert LAST <= 255, LAST
+O_A = lambda h, db: 64 * h + 16 * db
+OPITCH = 272
 SGPR = dict(T="s80", j="s81", kt="s82", kdlo="s84", kdhi="s85", vdlo="s86", vdhi="s87",
-            tk="s88", tv="s89", m="s[90:91]")
+            tk="s88", tv="s89", m="s[90:91]", m2="s[92:93]")
+
+
+INV = (RS[0], RS[1])   # 1/l after the loop (the sub-tile row sums are dead by then)
 
 
 def vr(b, n):
     return f"v[{b}:{b + n - 1}]"
 
 
+def ar(b, n):
+    return f"a[{b}:{b + n - 1}]"
+
+
 def slot_list(qk, pv):
-    """MFMA slots of one iteration: ('qk', ks) x 8 then ('pv', m2, db) x 8.  An
-    iteration without QK (the drain) has 'ghost' slots instead: the first LOOK
-    of them take the K reads the previous tile issued ahead (unused)."""
-    a = [("qk", ks) for ks in range(8)] if qk else [("ghost", ks) for ks in range(8)]
-    b = [("pv", m2, db) for m2 in range(2) for db in range(4)] if pv else []
+    a = [("qk", ks, h) for ks in range(8) for h in range(2)] if qk else \
+        [("ghost", ks, h) for ks in range(8) for h in range(2)]
+    b = [("pv", m2, db, h) for m2 in range(2) for db in range(4) for h in range(2)] if pv else []
     return a + b
 
 
 def has_reads(slot):
-    return slot[0] != "ghost" or slot[1] < LOOK
+    if slot[-1] != 0:
+        return False
+    return slot[0] != "ghost" or slot[1] < LOOK // 2
 
 
 def read_texts(slot, kbuf, vbuf, u):
     if slot[0] in ("qk", "ghost"):
         ks = slot[1]
-        return "k", [f"ds_read_b128 {{dst}}, v{100 + ks} offset:{kbuf * KT_BYTES + u * 8192}"]
+        return "k", [f"ds_read_b128 {{dst}}, v{KADDR + ks} offset:{kbuf * KT_BYTES + u * 8192}"]
     m2, db = slot[1], slot[2]
     off = vbuf * KT_BYTES + u * 8192 + m2 * 4096
-    return "v", [f"ds_read_b64_tr_b16 {{dlo}}, v{108 + db * 2} offset:{off}",
-                 f"ds_read_b64_tr_b16 {{dhi}}, v{108 + db * 2 + 1} offset:{off}"]
+    return "v", [f"ds_read_b64_tr_b16 {{dlo}}, v{VADDR + db * 2} offset:{off}",
+                 f"ds_read_b64_tr_b16 {{dhi}}, v{VADDR + db * 2 + 1} offset:{off}"]
 
 
-def softmax_ops(sbuf, pbuf):
-    """Vector ops of the softmax of one sub-tile: [kind, text, deps, ring reuse].
-    Row sum: v_add_f32 of the fp32 probabilities into two partial sums."""
+def softmax_ops(u):
+    """Vector ops of the softmax of sub-tile buffer u, both halves."""
     ops = []
     fid, eid, cid, aid = {}, {}, {}, {}
-    prev_add = {0: None, 1: None}
-    for r in range(16):
-        fid[r] = len(ops)
-        ops.append(["fma", f"v_fma_f32 v{F_RING + r % 6}, v{sbuf + r}, %[sc], v221", [], []])
-        eid[r] = len(ops)
-        ops.append(["exp", f"v_exp_f32 v{E_RING + r % 6}, v{F_RING + r % 6}", [fid[r]], []])
-        aid[r] = len(ops)
-        part = 225 + (r % 2)
-        if r < 2:
-            ops.append(["fma", f"v_mov_b32 v{part}, v{E_RING + r % 6}", [eid[r]], []])
-        else:
-            ops.append(["fma", f"v_add_f32 v{part}, v{part}, v{E_RING + r % 6}", [eid[r], prev_add[r % 2]], []])
-        prev_add[r % 2] = aid[r]
-        if r % 2 == 1:
-            k = r // 2
-            cid[k] = len(ops)
-            ops.append(["cvt", f"v_cvt_pk_bf16_f32 v{pbuf + k}, v{E_RING + (r - 1) % 6}, v{E_RING + r % 6}",
-                        [eid[r - 1], eid[r]], []])
-    ops.append(["fma", "v_add_f32 v220, v225, v226", [prev_add[0], prev_add[1]], []])
-    for r in range(6, 16):
-        ops[fid[r]][3].append(eid[r - 6])
-        ops[eid[r]][3].append(cid[(r - 6) // 2])
-        ops[eid[r]][3].append(aid[r - 6])
+    for h in range(2):
+        sb, pb = S_AT(u, h), P_AT(u, h)
+        prev = {0: None, 1: None}
+        for r in range(16):
+            i = 16 * h + r
+            fid[i] = len(ops)
+            ops.append(["fma", f"v_fma_f32 v{F_RING + i % NRING}, v{sb + r}, %[sc], v{NM[h]}", [], []])
+            eid[i] = len(ops)
+            ops.append(["exp", f"v_exp_f32 v{E_RING + i % NRING}, v{F_RING + i % NRING}", [fid[i]], []])
+            aid[i] = len(ops)
+            part = PART + 2 * h + (r % 2)
+            if r < 2:
+                ops.append(["fma", f"v_mov_b32 v{part}, v{E_RING + i % NRING}", [eid[i]], []])
+            else:
+                ops.append(["fma", f"v_add_f32 v{part}, v{part}, v{E_RING + i % NRING}", [eid[i], prev[r % 2]], []])
+            prev[r % 2] = aid[i]
+            if r % 2 == 1:
+                cid[i // 2] = len(ops)
+                ops.append(["cvt", f"v_cvt_pk_bf16_f32 v{pb + r // 2}, v{E_RING + (i - 1) % NRING}, "
+                                   f"v{E_RING + i % NRING}", [eid[i - 1], eid[i]], []])
+        ops.append(["fma", f"v_add_f32 v{RS[h]}, v{PART + 2 * h}, v{PART + 2 * h + 1}", [prev[0], prev[1]], []])
+    for i in range(NRING, 32):
+        ops[fid[i]][3].append(eid[i - NRING])
+        ops[eid[i]][3].append(cid[(i - NRING) // 2])
+        ops[eid[i]][3].append(aid[i - NRING])
     return ops
 
 
 def schedule(ops, nslots, budget=BUDGET):
-    """Cost-aware list schedule of ops into nslots slots (a dependence must
-    come from an earlier slot; a ring entry is rewritten only after its reader
-    is placed).  Whatever does not fit goes to the last slot."""
     where, per = {}, [[] for _ in range(nslots)]
     pending = list(range(len(ops)))
     s = 0
@@ -151,30 +188,29 @@ def schedule(ops, nslots, budget=BUDGET):
 class Gen:
     def __init__(self):
         self.L = []
-        self.ring_k = 0   # next K ring entry
+        self.ring_k = 0
         self.ring_v = 0
         self.fifo = []
         self.label_n = 0
         self.slow_blocks = []
+        self.cur = None
 
     def a(self, s):
         self.L.append(s)
 
     def label(self, base):
         self.label_n += 1
-        return f".Lhd{base}_{self.label_n}_%="
+        return f".Lhw{base}_{self.label_n}_%="
 
-    # ---- LDS read stream -------------------------------------------------
-    # fifo: reads issued for slots not yet executed, in order: (n_reads, target)
     def issue_reads(self, slot, kbuf, vbuf, u):
         kind, texts = read_texts(slot, kbuf, vbuf, u)
         if kind == "k":
-            b = 176 + 4 * self.ring_k
+            b = KRING + 4 * self.ring_k
             self.ring_k = (self.ring_k + 1) % RING
             self.a(texts[0].format(dst=vr(b, 4)))
             self.fifo.append((1, vr(b, 4)))
         else:
-            b = 192 + 4 * self.ring_v
+            b = VRING + 4 * self.ring_v
             self.ring_v = (self.ring_v + 1) % RING
             self.a(texts[0].format(dlo=vr(b, 2)))
             self.a(texts[1].format(dhi=vr(b + 2, 2)))
@@ -187,87 +223,103 @@ class Gen:
             self.a(f"s_waitcnt lgkmcnt({min(later, 15)})")
         return target
 
-    # ---- pieces ------------------------------------------------------------
-    def mask_block(self, sb):
-        """Scores of the sub-tile at key %[kt] outside the lane's band -> -inf."""
+    def mask_block(self, u):
         skip, do = self.label("nomask"), self.label("mask")
         self.a(f"s_cmp_lt_u32 {SGPR['j']}, %[jw]")
         self.a(f"s_cbranch_scc1 {do}")
         self.a(f"s_cmp_ge_u32 {SGPR['j']}, %[jm]")
         self.a(f"s_cbranch_scc0 {skip}")
         self.a(f"{do}:")
-        self.a(f"v_add_u32 v222, {SGPR['kt']}, v98")
-        for r in range(16):
-            c = 8 * (r >> 2) + (r & 3)
-            self.a(f"v_add_u32 v223, {c}, v222")
-            self.a("v_cmp_le_u32 vcc, v223, v99")
-            self.a("s_nop 4")
-            self.a(f"v_cndmask_b32 v{sb + r}, v229, v{sb + r}, vcc")
+        for h in range(2):
+            sb = S_AT(u, h)
+            self.a(f"v_add_u32 v{T}, {SGPR['kt']}, v{MB[h]}")
+            for r in range(16):
+                c = 8 * (r >> 2) + (r & 3)
+                self.a(f"v_add_u32 v{T + 1}, {c}, v{T}")
+                self.a(f"v_cmp_le_u32 vcc, v{T + 1}, v{SPAN[h]}")
+                self.a(CMPNOP)
+                self.a(f"v_cndmask_b32 v{sb + r}, v{NINF}, v{sb + r}, vcc")
         self.a(f"{skip}:")
 
-    def slow_path(self, sb, pb, back):
-        """The tile max, O and l rescale and the probabilities again (rare)."""
+    def slow_path(self, u, back):
+        """Tile max, O and l rescale, probabilities again, for both halves (rare)."""
         lab = self.label("slow")
         body = [f"{lab}:", "s_nop 7", "s_nop 7", "s_nop 7"]
-        body.append(f"v_max3_f32 v222, v{sb}, v{sb + 1}, v{sb + 2}")
-        for r in range(3, 16, 2):
-            if r + 1 < 16:
-                body.append(f"v_max3_f32 v222, v222, v{sb + r}, v{sb + r + 1}")
-            else:
-                body.append(f"v_max_f32 v222, v222, v{sb + r}")
-        body += ["v_mov_b32 v223, v222", "s_nop 1", "v_permlane32_swap_b32 v222, v223", "s_nop 1",
-                 "v_max_f32 v222, v222, v223",
-                 "v_mul_f32 v222, %[sc], v222",        # tile max in log2 units
-                 "v_max_f32 v223, v96, v222",          # new max
-                 "v_sub_f32 v224, v96, v223",
-                 "v_exp_f32 v224, v224",
-                 "v_cmp_eq_f32 vcc, v96, v223",
-                 "s_nop 4",
-                 "v_cndmask_b32_e64 v224, v224, 1.0, vcc"]  # alpha
-        body += [f"v_mul_f32 v{r}, v{r}, v224" for r in range(64)]
-        body += ["v_mul_f32 v97, v97, v224", "v_mov_b32 v96, v223",
-                 "v_sub_f32 v221, 0, v223",
-                 "v_cmp_eq_f32 vcc, v229, v223",
-                 "s_nop 4",
-                 "v_cndmask_b32_e64 v221, v221, 0, vcc"]
-        # probabilities of the sub-tile against the new max, in program order
-        for r in range(16):
-            body.append(f"v_fma_f32 v{F_RING + r % 6}, v{sb + r}, %[sc], v221")
-            body.append("s_nop 0")
-            body.append(f"v_exp_f32 v{E_RING + r % 6}, v{F_RING + r % 6}")
-            body.append("s_nop 0")
-            if r == 0:
-                body.append(f"v_mov_b32 v220, v{E_RING}")
-            else:
-                body.append(f"v_add_f32 v220, v220, v{E_RING + r % 6}")
-            if r % 2 == 1:
-                k = r // 2
-                body.append(f"v_cvt_pk_bf16_f32 v{pb + k}, v{E_RING + (r - 1) % 6}, v{E_RING + r % 6}")
-        body.append("s_nop 4")
-        body.append(f"s_branch {back}")
+        for h in range(2):
+            sb, pb = S_AT(u, h), P_AT(u, h)
+            t0, t1, t2 = T, T + 1, T + 2
+            body.append(f"v_max3_f32 v{t0}, v{sb}, v{sb + 1}, v{sb + 2}")
+            for r in range(3, 16, 2):
+                if r + 1 < 16:
+                    body.append(f"v_max3_f32 v{t0}, v{t0}, v{sb + r}, v{sb + r + 1}")
+                else:
+                    body.append(f"v_max_f32 v{t0}, v{t0}, v{sb + r}")
+            body += [f"v_mov_b32 v{t1}, v{t0}", "s_nop 1", f"v_permlane32_swap_b32 v{t0}, v{t1}", "s_nop 1",
+                     f"v_max_f32 v{t0}, v{t0}, v{t1}",
+                     f"v_mul_f32 v{t0}, %[sc], v{t0}",            # tile max in log2 units
+                     f"v_max_f32 v{t1}, v{M[h]}, v{t0}",          # new max
+                     f"v_sub_f32 v{t2}, v{M[h]}, v{t1}",
+                     f"v_exp_f32 v{t2}, v{t2}",
+                     f"v_cmp_eq_f32 vcc, v{M[h]}, v{t1}",
+                     "s_nop 4",
+                     f"v_cndmask_b32_e64 v{t2}, v{t2}, 1.0, vcc"]  # alpha
+            # O rescale only where a lane has a nonzero sum and alpha != 1
+            skip = self.label("norescale")
+            body += [f"v_cmp_neq_f32_e64 {SGPR['m']}, 0, v{L[h]}",
+                     f"v_cmp_neq_f32 vcc, 1.0, v{t2}",
+                     "s_nop 4",
+                     f"s_and_b64 vcc, vcc, {SGPR['m']}",
+                     "s_and_b64 vcc, vcc, exec",
+                     f"s_cbranch_vccz {skip}"]
+            for i0 in range(0, 64, 8):
+                for k in range(8):
+                    body.append(f"v_accvgpr_read_b32 v{F_RING + k}, a{64 * h + i0 + k}")
+                for k in range(8):
+                    body.append(f"v_mul_f32 v{F_RING + k}, v{F_RING + k}, v{t2}")
+                for k in range(8):
+                    body.append(f"v_accvgpr_write_b32 a{64 * h + i0 + k}, v{F_RING + k}")
+            body.append(f"{skip}:")
+            body += [f"v_mul_f32 v{L[h]}, v{L[h]}, v{t2}", f"v_mov_b32 v{M[h]}, v{t1}",
+                     f"v_sub_f32 v{NM[h]}, 0, v{t1}",
+                     f"v_cmp_eq_f32 vcc, v{NINF}, v{t1}",
+                     "s_nop 4",
+                     f"v_cndmask_b32_e64 v{NM[h]}, v{NM[h]}, 0, vcc"]
+            for r in range(16):
+                body.append(f"v_fma_f32 v{F_RING + r % 6}, v{sb + r}, %[sc], v{NM[h]}")
+                body.append("s_nop 0")
+                body.append(f"v_exp_f32 v{E_RING + r % 6}, v{F_RING + r % 6}")
+                body.append("s_nop 0")
+                if r == 0:
+                    body.append(f"v_mov_b32 v{RS[h]}, v{E_RING}")
+                else:
+                    body.append(f"v_add_f32 v{RS[h]}, v{RS[h]}, v{E_RING + r % 6}")
+                if r % 2 == 1:
+                    body.append(f"v_cvt_pk_bf16_f32 v{pb + r // 2}, v{E_RING + (r - 1) % 6}, v{E_RING + r % 6}")
+        body += ["s_nop 7", f"s_branch {back}"]
         self.slow_blocks.append(body)
         return lab
 
-    def check(self, sb, pb):
-        """Keep the fast probabilities unless some row has no max yet or a
-        lane's share of its row sum exceeds 2^32 (or is not a number)."""
+    def check(self, u):
         back = self.label("back")
-        slow = self.slow_path(sb, pb, back)
-        self.a("v_cmp_nge_f32 vcc, v230, v220")
-        self.a(f"v_cmp_eq_f32_e64 {SGPR['m']}, v229, v96")
-        self.a("s_nop 4")
+        slow = self.slow_path(u, back)
+        self.a(f"v_cmp_nge_f32 vcc, v{TWO32}, v{RS[0]}")
+        self.a(f"v_cmp_nge_f32_e64 {SGPR['m']}, v{TWO32}, v{RS[1]}")
+        self.a(f"v_cmp_eq_f32_e64 {SGPR['m2']}, v{NINF}, v{M[0]}")
+        self.a(CMPNOP)
+        self.a(f"s_or_b64 vcc, vcc, {SGPR['m']}")
+        self.a(f"s_or_b64 vcc, vcc, {SGPR['m2']}")
+        self.a(f"v_cmp_eq_f32_e64 {SGPR['m']}, v{NINF}, v{M[1]}")
+        self.a(CMPNOP)
         self.a(f"s_or_b64 vcc, vcc, {SGPR['m']}")
         self.a("s_and_b64 vcc, vcc, exec")
         self.a(f"s_cbranch_vccnz {slow}")
         self.a(f"{back}:")
-        self.a("v_add_f32 v97, v97, v220")
+        self.a(f"v_add_f32 v{L[0]}, v{L[0]}, v{RS[0]}")
+        self.a(f"v_add_f32 v{L[1]}, v{L[1]}, v{RS[1]}")
 
-    def iteration(self, u, kbuf, vbuf, qk, sm, pv, nxt, pre_nops=False):
-        """One sub-tile iteration i with u = i % 2: QK writes S[u], the softmax
-        reads S[1-u] and writes P[1-u], PV reads P[u].  nxt = (kbuf, vbuf, u, qk, pv)
-        of the iteration that follows (its first slots' reads are issued here)."""
-        sq, ss = S_BASE[u], S_BASE[1 - u]
-        ps, pp = P_BASE[1 - u], P_BASE[u]
+    def iteration(self, u, kbuf, vbuf, qk, sm, pv, nxt, pre_nops=False, extra=None):
+        """Sub-tile iteration with u = i % 2: QK writes S[u], the softmax reads
+        S[1-u] and writes P[1-u], PV reads P[u]."""
         slots = slot_list(qk, pv)
         nslots = slot_list(nxt[3], nxt[4])
         stream = [(s, kbuf, vbuf, u) for s in slots] + [(s, nxt[0], nxt[1], nxt[2]) for s in nslots]
@@ -276,32 +328,37 @@ class Gen:
             self.a("s_nop 7")
             self.a("s_nop 7")
         if sm:
-            self.mask_block(ss)
-        per = schedule(softmax_ops(ss, ps), len(slots)) if sm else [[] for _ in slots]
+            self.mask_block(1 - u)
+        per = schedule(softmax_ops(1 - u), len(slots)) if sm else [[] for _ in slots]
         first_pv = True
         for n, slot in enumerate(slots):
-            target = None
             if has_reads(slot):
-                target = self.take(wait=slot[0] != "ghost")
+                self.cur = self.take(wait=slot[0] != "ghost")
+            target = self.cur
             if slot[0] == "qk":
-                ks = slot[1]
-                src_c = "0" if ks == 0 else vr(sq, 16)
-                self.a(f"v_mfma_f32_32x32x16_bf16 {vr(sq, 16)}, {target}, {vr(64 + 4 * ks, 4)}, {src_c}")
+                ks, h = slot[1], slot[2]
+                d = vr(S_AT(u, h), 16)
+                src_c = "0" if ks == 0 else d
+                self.a(f"v_mfma_f32_32x32x16_bf16 {d}, {target}, {vr(Q_V(h, ks), 4)}, {src_c}")
             elif slot[0] == "pv":
-                m2, db = slot[1], slot[2]
+                m2, db, h = slot[1], slot[2], slot[3]
                 if first_pv and not qk:
                     self.a("s_nop 2")
                 first_pv = False
-                self.a(f"v_mfma_f32_32x32x16_bf16 {vr(16 * db, 16)}, {target}, {vr(pp + 4 * m2, 4)}, {vr(16 * db, 16)}")
+                o = ar(O_A(h, db), 16)
+                self.a(f"v_mfma_f32_32x32x16_bf16 {o}, {target}, {vr(P_AT(u, h) + 4 * m2, 4)}, {o}")
             ahead = n + LOOK
             if ahead < len(stream):
                 s2, kb2, vb2, u2 = stream[ahead]
                 if has_reads(s2):
                     self.issue_reads(s2, kb2, vb2, u2)
+            if extra and n in extra:
+                for t in extra[n]:
+                    self.a(t)
             for t in per[n]:
                 self.a(t)
         if sm:
-            self.check(ss, ps)
+            self.check(1 - u)
             self.a(f"s_add_u32 {SGPR['j']}, {SGPR['j']}, 1")
             self.a(f"s_add_u32 {SGPR['kt']}, {SGPR['kt']}, 32")
 
@@ -309,36 +366,40 @@ class Gen:
 def generate():
     g = Gen()
     a = g.a
-    # ---- set-up ---------------------------------------------------------------
-    a("v_mov_b32 v229, 0xff800000")
-    a("v_mov_b32 v230, 0x4f800000")
-    a("v_mov_b32 v221, 0")
+    # ---- set-up: O = 0, constants --------------------------------------------------
+    for i in range(128):
+        a(f"v_accvgpr_write_b32 a{i}, 0")
+    a(f"v_mov_b32 v{NINF}, 0xff800000")
+    a(f"v_mov_b32 v{TWO32}, 0x4f800000")
+    a(f"v_mov_b32 v{NM[0]}, 0")
+    a(f"v_mov_b32 v{NM[1]}, 0")
     a(f"s_mov_b32 {SGPR['T']}, 0")
     a(f"s_mov_b32 {SGPR['j']}, 0")
     a(f"s_mov_b32 {SGPR['kt']}, %[kt0]")
     a(f"s_mov_b64 s[{SGPR['kdlo'][1:]}:{SGPR['kdhi'][1:]}], %[kptr2]")
     a(f"s_mov_b64 s[{SGPR['vdlo'][1:]}:{SGPR['vdhi'][1:]}], %[vptr1]")
 
-    def dma(kind, buf, tail_idx_sgpr):
-        """Copy the tile at the running pointer into ring buffer `buf`, then
-        advance the pointer.  kind 'k' or 'v'."""
+    def dma(kind, buf, tail_idx_sgpr, out):
+        """Copy the tile at the running pointer into ring buffer `buf` (lines
+        appended to `out`), then advance the pointer.  kind 'k' or 'v'."""
+        a = out.append
         lo, hi = (SGPR['kdlo'], SGPR['kdhi']) if kind == "k" else (SGPR['vdlo'], SGPR['vdhi'])
         ring = 0 if kind == "k" else V_RING
-        offs = (116, 117) if kind == "k" else (118, 119)
-        toffs = (120, 121) if kind == "k" else (122, 123)
+        offs = CPK if kind == "k" else CPV
+        toffs = TPK if kind == "k" else TPV
         normal, done = g.label("dman"), g.label("dmad")
         a(f"s_cmp_eq_u32 {tail_idx_sgpr}, %[tailt]")
         a(f"s_cbranch_scc0 {normal}")
-        for i in range(2):
+        for i in range(4):
             a(f"s_add_u32 m0, %[ldsw], {ring + buf * KT_BYTES + i * 1024}")
             a("s_nop 0")
-            a(f"global_load_lds_dwordx4 v{toffs[i]}, s[{lo[1:]}:{hi[1:]}]")
+            a(f"global_load_lds_dwordx4 v{toffs + i}, s[{lo[1:]}:{hi[1:]}]")
         a(f"s_branch {done}")
         a(f"{normal}:")
-        for i in range(2):
+        for i in range(4):
             a(f"s_add_u32 m0, %[ldsw], {ring + buf * KT_BYTES + i * 1024}")
             a("s_nop 0")
-            a(f"global_load_lds_dwordx4 v{offs[i]}, s[{lo[1:]}:{hi[1:]}]")
+            a(f"global_load_lds_dwordx4 v{offs + i}, s[{lo[1:]}:{hi[1:]}]")
         a(f"{done}:")
         a(f"s_add_u32 {lo}, {lo}, %[tbytes]")
         a(f"s_addc_u32 {hi}, {hi}, 0")
@@ -348,107 +409,136 @@ def generate():
     a(f"s_mov_b32 {SGPR['tk']}, 2")
     a(f"s_mov_b32 {SGPR['tv']}, 1")
 
-    def header(p, first=False):
-        """Start of tile T (T % 3 == p): wait for the copies issued one tile
-        ago, barrier, copy K(T+2) and V(T+1)."""
+    def header(p):
+        """Start of tile T (T % 3 == p): wait for the K copies issued one
+        tile ago (the last 4 copies, of V, may stay in flight: V(T+1) is first
+        read in tile T+2), barrier; returns the copies of K(T+2) and V(T+1),
+        which the tile's first iteration issues after its MFMA slots 1 and 5."""
+        a = g.a
         nahead = sum(x[0] for x in g.fifo)
-        a("s_waitcnt vmcnt(0)")
+        a("s_waitcnt vmcnt(4)")
         a(f"s_waitcnt lgkmcnt({min(nahead, 15)})")
         a("s_barrier")
         nk, nv = g.label("nok"), g.label("nov")
-        a(f"s_cmp_lt_u32 {SGPR['tk']}, %[nt]")
-        a(f"s_cbranch_scc0 {nk}")
-        dma("k", (p + 2) % 3, SGPR['tk'])
-        a(f"{nk}:")
-        a(f"s_add_u32 {SGPR['tk']}, {SGPR['tk']}, 1")
-        a(f"s_cmp_lt_u32 {SGPR['tv']}, %[nt]")
-        a(f"s_cbranch_scc0 {nv}")
-        dma("v", (p + 1) % 3, SGPR['tv'])
-        a(f"{nv}:")
-        a(f"s_add_u32 {SGPR['tv']}, {SGPR['tv']}, 1")
+        kl, vl = [], []
+        kl.append(f"s_cmp_lt_u32 {SGPR['tk']}, %[nt]")
+        kl.append(f"s_cbranch_scc0 {nk}")
+        dma("k", (p + 2) % 3, SGPR['tk'], kl)
+        kl.append(f"{nk}:")
+        kl.append(f"s_add_u32 {SGPR['tk']}, {SGPR['tk']}, 1")
+        vl.append(f"s_cmp_lt_u32 {SGPR['tv']}, %[nt]")
+        vl.append(f"s_cbranch_scc0 {nv}")
+        dma("v", (p + 1) % 3, SGPR['tv'], vl)
+        vl.append(f"{nv}:")
+        vl.append(f"s_add_u32 {SGPR['tv']}, {SGPR['tv']}, 1")
+        return {1: kl, 5: vl}
 
-    def run_iter(kbuf, vbuf, u, qk, sm, pv, nxt, pre_nops=False):
-        g.iteration(u, kbuf, vbuf, qk, sm, pv, nxt, pre_nops=pre_nops)
+    def run_iter(kbuf, vbuf, u, qk, sm, pv, nxt, pre_nops=False, extra=None):
+        g.iteration(u, kbuf, vbuf, qk, sm, pv, nxt, pre_nops=pre_nops, extra=extra)
 
     def start_reads(kbuf, vbuf, u, qk, pv):
         for s in slot_list(qk, pv)[:LOOK]:
-            g.issue_reads(s, kbuf, vbuf, u)
+            if has_reads(s):
+                g.issue_reads(s, kbuf, vbuf, u)
 
-    # The stream of tiles: tile 0 (prologue iterations), then tiles T >= 1
-    # with parity T % 3, then the drain after the last tile.  Every tile ends
-    # with the reads of the next tile's first QK operands issued (for the drain
-    # they read a K buffer nobody uses: harmless).
     drain_labels = {p: g.label(f"drain{p}") for p in range(3)}
     tile_labels = {p: g.label(f"tile{p}") for p in range(3)}
 
-    # tile 0
-    header(0, first=True)
+    a("s_nop 7")   # AGPR writes before the first MFMA accumulates into them
+    ex0 = header(0)
     start_reads(0, 0, 0, True, False)
-    run_iter(0, 0, 0, True, False, False, (0, 0, 1, True, False))            # i = 0: QK(0)
-    run_iter(0, 0, 1, True, True, False, (1, 0, 0, True, True), pre_nops=True)  # i = 1: QK(1), softmax(0)
-    # iteration 1 has no PV MFMAs after its QK MFMAs: let them finish before
-    # the next softmax reads their scores
+    run_iter(0, 0, 0, True, False, False, (0, 0, 1, True, False), extra=ex0)
+    run_iter(0, 0, 1, True, True, False, (1, 0, 0, True, True), pre_nops=True)
     a("s_nop 7")
     a("s_nop 7")
     a("s_nop 7")
     a(f"s_add_u32 {SGPR['T']}, {SGPR['T']}, 1")
     a(f"s_cmp_eq_u32 {SGPR['T']}, %[nt]")
     a(f"s_cbranch_scc1 {drain_labels[0]}")
-    # steady tiles, parity 1, 2, 0, 1, ...
     for p in (1, 2, 0):
         a(f"{tile_labels[p]}:")
-        header(p)
+        ex = header(p)
         kb, vb = p, (p - 1) % 3
-        run_iter(kb, vb, 0, True, True, True, (kb, vb, 1, True, True))
+        run_iter(kb, vb, 0, True, True, True, (kb, vb, 1, True, True), extra=ex)
         run_iter(kb, vb, 1, True, True, True, ((p + 1) % 3, p, 0, True, True))
         a(f"s_add_u32 {SGPR['T']}, {SGPR['T']}, 1")
         a(f"s_cmp_eq_u32 {SGPR['T']}, %[nt]")
         a(f"s_cbranch_scc1 {drain_labels[p]}")
         a(f"s_branch {tile_labels[(p + 1) % 3]}")
     end = g.label("end")
-    # drains: the last tile had parity p; its V is in V buffer p
     saved = (list(g.fifo), g.ring_k, g.ring_v)
     for p in range(3):
         g.fifo, g.ring_k, g.ring_v = list(saved[0]), saved[1], saved[2]
         a(f"{drain_labels[p]}:")
+        a("s_waitcnt vmcnt(0)")   # V of the last tile
+        a("s_barrier")
         run_iter((p + 1) % 3, p, 0, False, True, True, ((p + 1) % 3, p, 1, False, True), pre_nops=True)
         run_iter((p + 1) % 3, p, 1, False, False, True, ((p + 1) % 3, p, 0, False, False), pre_nops=True)
         a(f"s_branch {end}")
     for blk in g.slow_blocks:
         g.L.extend(blk)
     a(f"{end}:")
+    # ---- epilogue: row sums over the lane pair, O / l to LDS staging ---------------
     a("s_waitcnt lgkmcnt(0)")
     a("s_nop 7")
     a("s_nop 7")
     a("s_nop 7")
+    for h in range(2):
+        a(f"v_mov_b32 v{T}, v{L[h]}")
+        a(f"v_mov_b32 v{T + 1}, v{L[h]}")
+        a("s_nop 1")
+        a(f"v_permlane32_swap_b32 v{T}, v{T + 1}")
+        a("s_nop 1")
+        a(f"v_add_f32 v{L[h]}, v{T}, v{T + 1}")
+        # 1/l: hardware reciprocal and one Newton step
+        a(f"v_rcp_f32 v{INV[h]}, v{L[h]}")
+        a("s_nop 0")
+        a(f"v_fma_f32 v{T}, -v{L[h]}, v{INV[h]}, 1.0")
+        a(f"v_fma_f32 v{INV[h]}, v{T}, v{INV[h]}, v{INV[h]}")
+    a("s_barrier")   # every wave has left the loop: the rings are free
+    n = 0
+    for h in range(2):
+        for db in range(4):
+            for r4 in range(4):
+                t = 4 * (n % 16)
+                n += 1
+                for e in range(4):
+                    a(f"v_accvgpr_read_b32 v{t + e}, a{O_A(h, db) + 4 * r4 + e}")
+                for e in range(4):
+                    a(f"v_mul_f32 v{t + e}, v{t + e}, v{INV[h]}")
+                a(f"v_cvt_pk_bf16_f32 v{t}, v{t}, v{t + 1}")
+                a(f"v_cvt_pk_bf16_f32 v{t + 1}, v{t + 2}, v{t + 3}")
+                a(f"ds_write_b64 v{STG}, v[{t}:{t + 1}] offset:{h * 32 * OPITCH + db * 64 + r4 * 16}")
+    a("s_waitcnt lgkmcnt(0)")
     return g.L
 
 
 def trans_gaps(lines):
-    """A vector op that reads the result of the transcendental op just before
-    it needs one wait state (gfx950): insert s_nop 0 there."""
     out = []
     for ln in lines:
-        if out and out[-1].startswith("v_exp_f32"):
+        if out and (out[-1].startswith("v_exp_f32") or out[-1].startswith("v_rcp_f32")):
             dst = out[-1].split()[1].rstrip(",")
             ops = ln.replace(",", " ").split()[1:]
-            if ln.startswith("v_") and dst in ops[1:] if not ln.startswith("v_dot2c") else dst in ops:
+            if ln.startswith("v_") and (dst in ops[1:] or ("-" + dst) in ops[1:]):
                 out.append("s_nop 0")
         out.append(ln)
     return out
 
 
 if __name__ == "__main__":
+    out_path = sys.argv[sys.argv.index("--out") + 1] if "--out" in sys.argv else \
+        os.path.join(os.path.dirname(os.path.abspath(__file__)), "sfa_fwd_d128_loop.inc")
     lines = trans_gaps(generate())
-    here = os.path.dirname(os.path.abspath(__file__))
-    with open(os.path.join(here, "sfa_fwd_d128_loop.inc"), "w") as f:
+    with open(out_path, "w") as f:
         f.write("// Generated by gen_fwd_d128_loop.py: the key-tile loop of the head-dim-128\n")
         f.write("// prefill as one instruction stream (see that script for the register map).\n")
         f.write("#define HD_FWD_D128_LOOP \\\n")
         for ln in lines:
             f.write('    "' + ln + '\\n\\t" \\\n')
         f.write('    ""\n')
-        clob = ([f'"v{i}"' for i in range(128, 231)] + [f'"s{i}"' for i in range(80, 94)] +
+        clob = ([f'"v{i}"' for i in list(range(0, 96)) + list(range(KRING, STG))] +
+                [f'"a{i}"' for i in range(128)] +
+                [f'"s{i}"' for i in range(80, 94)] +
                 ['"vcc"', '"m0"', '"scc"', '"memory"'])
         f.write("#define HD_FWD_D128_CLOBBERS " + ", ".join(clob) + "\n")
     print(len(lines), "lines")

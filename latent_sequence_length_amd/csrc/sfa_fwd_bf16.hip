@@ -224,17 +224,22 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 
 // ---------------------------------------------------------------------------
 // Head dim 128 fast path.  Same math as above, with these changes:
-//   * a workgroup is 8 waves (HG heads x 8/HG blocks of 32 positions), two
-//     per SIMD and one workgroup per CU, so every K/V tile copied into LDS
-//     serves 256 query rows (half the L2-to-LDS traffic of 4-wave groups);
+//   * a workgroup is 4 waves, one per SIMD and one workgroup per CU; a wave
+//     holds 64 queries of one head (two 32-query halves), the workgroup HG
+//     heads x 4/HG blocks of 64 positions, so every K/V tile copied into LDS
+//     serves 256 query rows, and every K or V^T fragment a wave reads from
+//     LDS feeds two MFMAs (one per half): half the LDS operand traffic of
+//     32-query waves.  O^T of both halves (128 accumulators) lives in AGPRs,
+//     the scores, probabilities and Q in VGPRs (an MFMA whose A or B operand
+//     is an AGPR gains nothing here, and accumulators in AGPRs cost nothing);
 //   * the key loop is one hand-ordered instruction stream (see
 //     gen_fwd_d128_loop.py): per 32-key sub-tile i, the QK^T MFMAs of i, the
 //     softmax of i-1 and the PV MFMAs of i-2, the softmax's vector ops placed
 //     one by one between the MFMAs so that the vector ALU and the matrix core
-//     of a SIMD work at the same time inside each wave;
+//     of the SIMD work at the same time inside the one wave;
 //   * K and V tiles are fetched with direct-to-LDS 16-byte loads
 //     (global_load_lds) into three-deep rings, one barrier per tile: K of
-//     tile t+2 and V of tile t+1 are in flight while tile t is computed, so a
+//     tile t+2 and V of tile t+1 are copied while tile t is computed, so a
 //     tile's first operand reads can be issued before its barrier; no VGPRs
 //     are spent on staging, and each lane's copy offset is fixed;
 //   * LDS rows are 256 B with the 16-byte chunk index XOR-swizzled by the row
@@ -253,11 +258,12 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //     sub-tile, the wave takes the tile max, rescales O and l and recomputes.
 //     The row sum l adds the fp32 probabilities (v_add_f32: the packed bf16
 //     dot instruction would stall the matrix core);
-//   * the output goes through LDS so that every store writes 16-byte pieces
-//     of whole rows;
+//   * the loop's last step scales O by 1/l and writes the bf16 rows to LDS,
+//     so that every global store writes 16-byte pieces of whole rows;
 //   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
 //     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
-constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
+constexpr int D128_NW = 4;  // waves per workgroup of the head-dim-128 kernel (one per SIMD)
+constexpr int D128_QW = 64; // queries per wave (two 32-query halves)
 
 
 // GQ: the query map is not the identity (qmul, qadd) != (1, 0); a full layer
@@ -265,7 +271,8 @@ constexpr int D128_NW = 8;  // waves per workgroup of the head-dim-128 kernel
 // ROPE: q is rotated at its expanded position right after the load.
 // This function does the work-item map, loads Q, builds the per-lane LDS
 // address tables and copy offsets the key loop (sfa_fwd_d128_loop.inc) uses,
-// binds them to the registers the loop expects, and writes the output.
+// binds them to the registers the loop expects, and stores the output rows
+// the loop leaves in LDS.
 template <bool GQ, bool ROPE>
 __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdArgs p, int HG, int TB, int nqblk,
                                                                   float scale_log2) {
@@ -306,17 +313,14 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const int kvh = rest % p.Hkv;
     const int b = rest / p.Hkv;
 
-    const int QB = QW * TB;
+    const int QB = D128_QW * TB;
     const int q0 = qblk * QB;
     const int hw = wave % HG, tb = wave / HG;
     const int h = kvh * g + hgrp * HG + hw;
-    const int qw0 = q0 + tb * QW;
-    const int myq = qw0 + l32;
-    const bool qvalid = myq < p.Lq;
+    const int qw0 = q0 + tb * D128_QW;      // first query of this wave; half hf holds qw0 + 32 hf + l32
     const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
-    const int mylim = myq * qmul + qadd;            // last key this query may see
-    const int lim0 = qw0 * qmul + qadd;             // ... for the wave's first query
-    const int lim1 = (qw0 + QW - 1) * qmul + qadd;  // ... and its last
+    const int lim0 = qw0 * qmul + qadd;                    // last key the wave's first query may see
+    const int lim1 = (qw0 + D128_QW - 1) * qmul + qadd;    // ... and its last
 
     const int64_t qrs = (int64_t)p.Hq * D;
     const int64_t krs = (int64_t)p.Hkv * D;
@@ -350,18 +354,18 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
                                      16 * (4 * (db ^ r4) + ((2 * g2 + c1) ^ (2 * jh + hi))) + 8 * c0;
     }
 
-    // Copies: each wave moves 2 x 1 KB of K and of V per tile: slots
-    // w*128 .. +127, slot s = row*16 + physical chunk; lane l of copy i fills
-    // slot (w*2+i)*64 + l with logical chunk (s%16) ^ sw(row).  A tile with
+    // Copies: each wave moves 4 x 1 KB of K and of V per tile: slots
+    // w*256 .. +255, slot s = row*16 + physical chunk; lane l of copy i fills
+    // slot (w*4+i)*64 + l with logical chunk (s%16) ^ sw(row).  A tile with
     // rows past the end of the sub-sequence re-reads its last row there
     // (finite data, masked in the loop).
     const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
-    unsigned boff[2], boffv[2], toff[2], toffv[2];
+    unsigned boff[4], boffv[4], toff[4], toffv[4];
     const int tlast = tfirst + (ntiles - 1) * KT;
     const int rmax = p.Lsub - 1 - tlast;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int lrow = (wave * 2 + i) * 4 + (lane >> 4);
+    for (int i = 0; i < 4; ++i) {
+        const int lrow = (wave * 4 + i) * 4 + (lane >> 4);
         const int lc = ((lane & 15) ^ swz128(lrow)) * 8, lcv = ((lane & 15) ^ swzv(lrow)) * 8;
         boff[i] = (unsigned)(lrow * rstride + lc) * 2u;
         boffv[i] = (unsigned)(lrow * rstride + lcv) * 2u;
@@ -373,92 +377,93 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     const void *kptr = static_cast<const bf16 *>(p.k) + tile0;
     const void *vptr = static_cast<const bf16 *>(p.v) + tile0;
     const unsigned tbytes = (unsigned)(KT * rstride) * 2u;
-    const unsigned ldsw = ldsk + (unsigned)wave * 2048u;  // this wave's copy slots in a ring buffer
+    const unsigned ldsw = ldsk + (unsigned)wave * 4096u;  // this wave's copy slots in a ring buffer
 
     // Copies of K(0), K(1) and V(0), in flight while Q is loaded; the loop
     // copies K(T+2) and V(T+1) at the start of tile T.
     if (ntiles > 0) {
         const char *k0 = static_cast<const char *>(kptr), *v0 = static_cast<const char *>(vptr);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16_s(k0, tailt == 0 ? toff[i] : boff[i], ldsw + i * 1024);
+        for (int i = 0; i < 4; ++i) lds_dma16_s(k0, tailt == 0 ? toff[i] : boff[i], ldsw + i * 1024);
         if (ntiles > 1) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
                 lds_dma16_s(k0 + tbytes, tailt == 1 ? toff[i] : boff[i], ldsw + TILE + i * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) lds_dma16_s(v0, tailt == 0 ? toffv[i] : boffv[i], ldsw + 3 * TILE + i * 1024);
+        for (int i = 0; i < 4; ++i) lds_dma16_s(v0, tailt == 0 ? toffv[i] : boffv[i], ldsw + 3 * TILE + i * 1024);
     }
     const void *kptr2 = static_cast<const char *>(kptr) + 2 * (size_t)tbytes;
     const void *vptr1 = static_cast<const char *>(vptr) + tbytes;
 
-    bf16x8 qop[D / 16];
-    {
+    // Q of both halves and each half's band: key
+    // k visible <=> k - lo <= span (unsigned).
+    bf16x8 qop[2][D / 16];
+    int maskbase[2], span[2], lo[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int myq = qw0 + 32 * hf + l32;
+        const bool qvalid = myq < p.Lq;
+        const int mylim = myq * qmul + qadd;
         const bf16 *qp = static_cast<const bf16 *>(p.q) + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs +
                          (int64_t)h * D;
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
             bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
-            qop[ks] = qvalid ? x : bf16x8{};
+            qop[hf][ks] = qvalid ? x : bf16x8{};
         }
-        // expanded position of the query: key element lim(p) of this sub-sequence
-        if (ROPE) rope_rotate_q<D>(qop, p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
+        if (ROPE) rope_rotate_q<D>(qop[hf], p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
+        lo[hf] = p.weff ? mylim - p.weff + 1 : 0;
+        span[hf] = min(mylim, p.Lsub - 1) - lo[hf];
+        maskbase[hf] = 4 * hi - lo[hf];
     }
-
-
-    // Band of this lane (key k visible <=> k - lo <= span, unsigned) and the
-    // wave's 32-key sub-tiles that need the mask: j < jw (window start) or
-    // j >= jm (the diagonal or the end of the sub-sequence).
-    const int lo = p.weff ? mylim - p.weff + 1 : 0;
-    const int span = min(mylim, p.Lsub - 1) - lo;
-    const int maskbase = 4 * hi - lo;
+    // The wave's 32-key sub-tiles that need the mask: j < jw (window start)
+    // or j >= jm (the diagonal or the end of the sub-sequence).
     const int mfull = min(lim0, p.Lsub - 1) - 31 - tfirst;
     const int jm = mfull >= 0 ? mfull / 32 + 1 : 0;
     const int wfull = lim1 - p.weff - tfirst;
     const int jw = (p.weff && wfull >= 0) ? wfull / 32 + 1 : 0;
-    f32x16 o0 = {}, o1 = {}, o2 = {}, o3 = {};
-    float m_run = -INFINITY, l_run = 0.f;
+
+    // The 64 output rows of this wave are staged in LDS (free once every wave
+    // has left the loop) so that each store writes 16-byte pieces of whole
+    // 256-byte rows.
+    constexpr int OPITCH = 272;  // bytes per staged row (16-byte aligned, spreads the banks)
+    char *ost = lds + wave * D128_QW * OPITCH;
+    const unsigned stg = lds_addr(ost) + l32 * OPITCH + 8 * hi;
+    float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
     if (ntiles > 0) {
         asm volatile(HD_FWD_D128_LOOP
-                     : "+{v[0:15]}"(o0), "+{v[16:31]}"(o1), "+{v[32:47]}"(o2), "+{v[48:63]}"(o3), "+{v96}"(m_run),
-                       "+{v97}"(l_run)
-                     : "{v[64:67]}"(qop[0]), "{v[68:71]}"(qop[1]), "{v[72:75]}"(qop[2]), "{v[76:79]}"(qop[3]),
-                       "{v[80:83]}"(qop[4]), "{v[84:87]}"(qop[5]), "{v[88:91]}"(qop[6]), "{v[92:95]}"(qop[7]),
-                       "{v98}"(maskbase), "{v99}"(span), "{v100}"(kaddr[0]), "{v101}"(kaddr[1]),
-                       "{v102}"(kaddr[2]), "{v103}"(kaddr[3]), "{v104}"(kaddr[4]), "{v105}"(kaddr[5]),
-                       "{v106}"(kaddr[6]), "{v107}"(kaddr[7]), "{v108}"(vaddr[0]), "{v109}"(vaddr[1]),
-                       "{v110}"(vaddr[2]), "{v111}"(vaddr[3]), "{v112}"(vaddr[4]), "{v113}"(vaddr[5]),
-                       "{v114}"(vaddr[6]), "{v115}"(vaddr[7]), "{v116}"(boff[0]), "{v117}"(boff[1]),
-                       "{v118}"(boffv[0]), "{v119}"(boffv[1]), "{v120}"(toff[0]), "{v121}"(toff[1]),
-                       "{v122}"(toffv[0]), "{v123}"(toffv[1]), [nt] "s"(ntiles), [kt0] "s"(tfirst),
-                       [kptr2] "s"(kptr2), [vptr1] "s"(vptr1), [tbytes] "s"(tbytes), [tailt] "s"(tailt), [jw] "s"(jw),
-                       [jm] "s"(jm), [sc] "s"(scale_log2), [ldsw] "s"(ldsw)
+                     : "+{v160}"(m0), "+{v161}"(m1), "+{v162}"(l0), "+{v163}"(l1)
+                     : "{v[96:99]}"(qop[0][0]), "{v[100:103]}"(qop[0][1]), "{v[104:107]}"(qop[0][2]),
+                       "{v[108:111]}"(qop[0][3]), "{v[112:115]}"(qop[0][4]), "{v[116:119]}"(qop[0][5]),
+                       "{v[120:123]}"(qop[0][6]), "{v[124:127]}"(qop[0][7]), "{v[128:131]}"(qop[1][0]),
+                       "{v[132:135]}"(qop[1][1]), "{v[136:139]}"(qop[1][2]), "{v[140:143]}"(qop[1][3]),
+                       "{v[144:147]}"(qop[1][4]), "{v[148:151]}"(qop[1][5]), "{v[152:155]}"(qop[1][6]),
+                       "{v[156:159]}"(qop[1][7]),
+                       "{v164}"(kaddr[0]), "{v165}"(kaddr[1]), "{v166}"(kaddr[2]), "{v167}"(kaddr[3]),
+                       "{v168}"(kaddr[4]), "{v169}"(kaddr[5]), "{v170}"(kaddr[6]), "{v171}"(kaddr[7]),
+                       "{v172}"(vaddr[0]), "{v173}"(vaddr[1]), "{v174}"(vaddr[2]), "{v175}"(vaddr[3]),
+                       "{v176}"(vaddr[4]), "{v177}"(vaddr[5]), "{v178}"(vaddr[6]), "{v179}"(vaddr[7]),
+                       "{v180}"(boff[0]), "{v181}"(boff[1]), "{v182}"(boff[2]), "{v183}"(boff[3]),
+                       "{v184}"(boffv[0]), "{v185}"(boffv[1]), "{v186}"(boffv[2]), "{v187}"(boffv[3]),
+                       "{v188}"(toff[0]), "{v189}"(toff[1]), "{v190}"(toff[2]), "{v191}"(toff[3]),
+                       "{v192}"(toffv[0]), "{v193}"(toffv[1]), "{v194}"(toffv[2]), "{v195}"(toffv[3]),
+                       "{v196}"(maskbase[0]), "{v197}"(maskbase[1]), "{v198}"(span[0]), "{v199}"(span[1]),
+                       "{v249}"(stg), [nt] "s"(ntiles), [kt0] "s"(tfirst), [kptr2] "s"(kptr2),
+                       [vptr1] "s"(vptr1), [tbytes] "s"(tbytes), [tailt] "s"(tailt), [jw] "s"(jw), [jm] "s"(jm),
+                       [sc] "s"(scale_log2), [ldsw] "s"(ldsw)
                      : HD_FWD_D128_CLOBBERS);
+    } else {
+        // no key tile (an empty key range): zero rows
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                *reinterpret_cast<uint2 *>(ost + (hf * 32 + l32) * OPITCH + 8 * hi + 16 * i) = uint2{0, 0};
+        __builtin_amdgcn_s_waitcnt(0xc07f);
     }
-
-    const float l_tot = pair_sum(l_run);
-    const float inv = 1.f / l_tot;
-    // The wave's 32 output rows go through LDS (free once every wave has left
-    // the loop), so that each store writes 16-byte pieces of whole 256-byte
-    // rows (16 lanes per row) instead of 8 bytes in each of 32 rows.
-    __syncthreads();
-    constexpr int OPITCH = 272;  // bytes per staged row (16-byte aligned, spreads the banks)
-    char *ost = lds + wave * QW * OPITCH;
-    {
-        const f32x16 oacc[4] = {o0, o1, o2, o3};
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                bf16x4 y;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) y[e] = (bf16)(oacc[db][4 * r4 + e] * inv);
-                *reinterpret_cast<bf16x4 *>(ost + l32 * OPITCH + (db * 32 + 8 * r4 + 4 * hi) * 2) = y;
-            }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's staged rows are in LDS
-#pragma unroll
-    for (int i = 0; i < QW / 4; ++i) {
+    for (int i = 0; i < D128_QW / 4; ++i) {
         const int row = 4 * i + (lane >> 4), c = lane & 15;
         const uint4 x = *reinterpret_cast<const uint4 *>(ost + row * OPITCH + c * 16);
         const int q = qw0 + row;
@@ -467,9 +472,16 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
             *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(p.o) + (qrow * qrs + (int64_t)h * D) * 2 + c * 16) = x;
         }
     }
-    if (qvalid && p.lse != nullptr && hi == 0) {
-        const int64_t qrow = qbase + (int64_t)myq * p.qstride;
-        p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] = m_run * kLn2 + __logf(l_tot);
+    if (p.lse != nullptr && hi == 0) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int myq = qw0 + 32 * hf + l32;
+            if (myq < p.Lq) {
+                const int64_t qrow = qbase + (int64_t)myq * p.qstride;
+                p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] =
+                    (hf ? m1 : m0) * kLn2 + __logf(hf ? l1 : l0);
+            }
+        }
     }
 }
 
@@ -498,7 +510,7 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
             }
             {
                 const int TB2 = D128_NW / HG;
-                const int nqblk2 = (a.Lq + QW * TB2 - 1) / (QW * TB2);
+                const int nqblk2 = (a.Lq + D128_QW * TB2 - 1) / (D128_QW * TB2);
                 const int64_t grid2 = (int64_t)nqblk2 * a.B * a.Hkv * (g / HG) * a.nsub;
                 if (grid2 > 0x7fffffff) return hipErrorInvalidConfiguration;
                 const bool gq = a.qmul != 1 || a.qadd != 0;

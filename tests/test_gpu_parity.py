@@ -148,6 +148,8 @@ BF16_SHAPES = [
     ((3, 1, 4, 4, 1, 128), INTRA, 0),       # one token
     ((1, 1, 1, 2, 1, 64), CROSS, 0),        # one position
     ((1, 129, 3, 4, 2, 128), CROSS, 1000),  # window wider than the sequence
+    ((2, 40, 4, 8, 2, 128), INTRA, 0),      # 64-query waves whose second half is partly past the end
+    ((1, 97, 2, 4, 1, 128), CROSS, 45),     # window edges in different sub-tiles for the two halves
 ]
 
 
