@@ -289,9 +289,10 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     // XCDs (XCD bid % 8 runs its workgroups in bid order); the map keeps each
     // XCD's share balanced (longest blocks first) and its groups few:
     // whole groups per XCD when the group count is a multiple of 8 (the
-    // XCD's groups interleaved, so its longest blocks of every group run
-    // first), each group spread over 8/G XCDs when G divides 8, else
-    // round-robin.
+    // XCD's groups taken two at a time, their blocks interleaved longest
+    // first: one group at a time leaves a tail of short blocks, all of them
+    // at once a K/V working set larger than the XCD's L2), each group spread
+    // over 8/G XCDs when G divides 8, else round-robin.
     const int nrest = p.B * p.Hkv * ngrp * p.nsub;
     const int nwg = nrest * nqblk;
     const int bid = blockIdx.x;
@@ -300,7 +301,9 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
         const int x = bid % 8, j = bid / 8;
         if (nrest % 8 == 0) {
             const int gpx = nrest / 8;
-            lid = (x * gpx + j % gpx) * nqblk + j / gpx;
+            const int iw = gpx % 2 == 0 ? 2 : gpx;  // groups interleaved at a time
+            const int ph = j / (iw * nqblk), jj = j % (iw * nqblk);
+            lid = (x * gpx + ph * iw + jj % iw) * nqblk + jj / iw;
         } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
             const int r = 8 / nrest;
             lid = (x / r) * nqblk + j * r + x % r;
