@@ -25,7 +25,13 @@ from latent_sequence_length_amd import hd, synth
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 INTRA, CROSS = 0, 1
-LSE_TOL_BF16 = 4e-3
+# The bf16 kernels sum the fp32 probabilities for l (lse = m + ln l): the
+# bar is the worst case of sequential fp32 summation over up to 4096
+# 32-key sub-tile sums (131072-key rows: 4096 * 2^-24 = 2.5e-4 relative in
+# l, the same absolute in lse), plus fp32 accumulation of the 128-term
+# scores (<= 128 * 2^-24 * sum|q_i k_i| * scale, ~6e-5 for unit-variance
+# inputs) and the exp2 / log / scale roundings (~1e-6).
+LSE_TOL_BF16 = 5e-4
 
 
 @pytest.fixture(autouse=True)
