@@ -501,6 +501,18 @@ def main():
             by = 2 * (2 * q.numel() + 3 * k.numel() + v.numel())
             comps["rope_fwd_intra_n4"] = (lambda q=q, k=k, v=v, o=o, kr=k_rot:
                                           hd.hd_sfa_fwd_rope(q, k, v, o, kr, I.n, I.mode), fl, by)
+        if want("intra_n4_const_inputs"):
+            # the headline layer on constant inputs (every element 0.25): the
+            # same instructions and memory traffic as intra_n4, so the rate
+            # difference is what the operands' switching costs in power and
+            # clock.  Reported beside the headline, never as it.
+            q, k, v = (torch.full((I.B, I.n * I.L, hh, I.d), 0.25, dtype=I.dtype, device=dev)
+                       for hh in (I.Hq, I.Hkv, I.Hkv))
+            o = torch.empty_like(q)
+            fl = useful_flops(I.B, I.L, I.n, I.Hq, I.d, I.mode, I.window)
+            by = 2 * (2 * q.numel() + k.numel() + v.numel())
+            comps["intra_n4_const_inputs"] = (lambda q=q, k=k, v=v, o=o: hd.hd_sfa_fwd(q, k, v, o, I.n, I.mode,
+                                                                                        I.window), fl, by)
     if "copy" in only:
         # calibration only, never part of the step: a plain elementwise copy
         # of 512 MiB, which reads and writes exactly that many bytes; its HBM
