@@ -6,12 +6,19 @@ then hd_sfa_bwd consumes them; the oracle computes its own forward and
 gradients in double from the same seeded q, k, v, dO.  Bars:
   - float32: max |gpu - oracle| <= 1e-4 * max(1, max |oracle|);
   - bf16: max |gpu - oracle| <= 2e-2 * max(1, max |oracle|) and
-          mean |gpu - oracle| <= 2e-3 * max(1, mean |oracle|).
+          mean |gpu - oracle| <= 4e-3 * max(1, mean |oracle|).
     Every gradient term carries at most two bf16 roundings (P or dS as an
     MFMA operand, each <= 2^-8 relative: bf16 carries 8 significant bits) on top of fp32 accumulation, and the
     output is rounded once more; D = dO . o uses the bf16 forward output.
-    The normalised bar is the forward's (2e-2 / 2e-3) scaled by the size of
-    the gradient, since dK and dV sum over many queries and heads.
+    The max bar is the forward's (2e-2) scaled by the size of the gradient,
+    since dK and dV sum over many queries and heads.
+    Mean bar: the arithmetic a bf16 backward must do rounds each P or dS
+    operand and each output to bf16 (unit roundoff u = 2^-8); averaged over
+    the elements the output rounding is about u/4 of the gradient's size and
+    the operand rounding, random in sign over the summed terms, about
+    u/(2 sqrt 3); their sum stays below u, so mean <= 4e-3 * max(1, mean |oracle|).
+    An exact emulation of just these two roundings gives 2.1e-3 on a
+    17-token, 3-stream, 8-head layer (few terms per sum).
 Small shapes are compared on every element; the full 4096-token workload on
 sampled rows plus the row-sum invariants over all keys.
 """
@@ -36,6 +43,9 @@ def announce(request):
     sys.__stdout__.flush()
     yield
     torch.cuda.synchronize()
+
+
+BWD_MEAN_BF16 = 4e-3  # mean bar for bf16 gradients (see the module docstring)
 
 
 def to_np(t):
@@ -107,18 +117,18 @@ def test_bwd_bf16_vs_oracle(shape, mode, window):
     q, k, v, dout, dq, dk, dv = run_fwd_bwd(shape, mode, window, torch.bfloat16)
     wq, wk, wv = oracle.sfa_bwd(q.cpu(), k.cpu(), v.cpu(), dout.cpu(), shape[2], mode, window)
     tag = f"{shape} mode={mode} W={window}"
-    check_grad(dq, wq, f"dq {tag}", 2e-2, 2e-3)
-    check_grad(dk, wk, f"dk {tag}", 2e-2, 2e-3)
-    check_grad(dv, wv, f"dv {tag}", 2e-2, 2e-3)
+    check_grad(dq, wq, f"dq {tag}", 2e-2, BWD_MEAN_BF16)
+    check_grad(dk, wk, f"dk {tag}", 2e-2, BWD_MEAN_BF16)
+    check_grad(dv, wv, f"dv {tag}", 2e-2, BWD_MEAN_BF16)
 
 
 def test_bwd_bf16_custom_scale():
     shape = (1, 70, 2, 4, 2, 64)
     q, k, v, dout, dq, dk, dv = run_fwd_bwd(shape, CROSS, 0, torch.bfloat16, scale=0.05)
     wq, wk, wv = oracle.sfa_bwd(q.cpu(), k.cpu(), v.cpu(), dout.cpu(), 2, CROSS, 0, 0.05)
-    check_grad(dq, wq, "dq", 2e-2, 2e-3)
-    check_grad(dk, wk, "dk", 2e-2, 2e-3)
-    check_grad(dv, wv, "dv", 2e-2, 2e-3)
+    check_grad(dq, wq, "dq", 2e-2, BWD_MEAN_BF16)
+    check_grad(dk, wk, "dk", 2e-2, BWD_MEAN_BF16)
+    check_grad(dv, wv, "dv", 2e-2, BWD_MEAN_BF16)
 
 
 def test_bwd_full_size_sampled():
@@ -140,9 +150,9 @@ def test_bwd_full_size_sampled():
     stats = oracle.row_stats(qc, kc, vc, dc, c.n, c.mode, c.window)
     wq, wk, wv = oracle.sfa_bwd_rows(qc, kc, vc, dc, c.n, c.mode, c.window, qrows=qrows, krows=krows,
                                      stats=stats)
-    check_grad(dq.reshape(-1, c.d)[torch.from_numpy(qrows).to(DEV)], wq, "dq rows", 2e-2, 2e-3)
-    check_grad(dk.reshape(-1, c.d)[torch.from_numpy(krows).to(DEV)], wk, "dk rows", 2e-2, 2e-3)
-    check_grad(dv.reshape(-1, c.d)[torch.from_numpy(krows).to(DEV)], wv, "dv rows", 2e-2, 2e-3)
+    check_grad(dq.reshape(-1, c.d)[torch.from_numpy(qrows).to(DEV)], wq, "dq rows", 2e-2, BWD_MEAN_BF16)
+    check_grad(dk.reshape(-1, c.d)[torch.from_numpy(krows).to(DEV)], wk, "dk rows", 2e-2, BWD_MEAN_BF16)
+    check_grad(dv.reshape(-1, c.d)[torch.from_numpy(krows).to(DEV)], wv, "dv rows", 2e-2, BWD_MEAN_BF16)
     # invariants over all keys of each (kv head, stream)
     dk64 = dk.double().reshape(c.B, c.L, c.n, c.Hkv, c.d)
     dv64 = dv.double().reshape(c.B, c.L, c.n, c.Hkv, c.d)
