@@ -564,7 +564,8 @@ def main():
     report = {}
     for name, (fn, fl, by) in comps.items():
         t = float(np.mean(timer.ms[name]))
-        report[name] = {"ms": round(t, 4), "ms_min": round(float(np.min(timer.ms[name])), 4)}
+        report[name] = {"ms": round(t, 4), "ms_min": round(float(np.min(timer.ms[name])), 4),
+                        "ms_median": round(float(np.median(timer.ms[name])), 4)}
         if fl:
             report[name]["TFLOP/s"] = round(fl / t / 1e9, 2)
         report[name]["GB/s"] = round(by / t / 1e6, 1)

@@ -97,6 +97,9 @@ def test_bench_json_line():
         assert isinstance(d.get(key), typ), (key, d.get(key))
     assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0
     assert "workload" in d["config"]
+    for name, comp in d["components"].items():  # mean, min and median of every timed row
+        assert {"ms", "ms_min", "ms_median"} <= set(comp), name
+        assert comp["ms_min"] <= comp["ms_median"] + 1e-9, name
     roof = d["roofline"]
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in roof, key
