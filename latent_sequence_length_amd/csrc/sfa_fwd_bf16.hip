@@ -266,9 +266,28 @@ constexpr int D128_NW = 4;  // waves per workgroup of the head-dim-128 kernel (o
 constexpr int D128_QW = 64; // queries per wave (two 32-query halves)
 
 
+// A wave-uniform pointer, marked so for the compiler.
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (const char *)(((uint64_t)hi << 32) | lo);
+}
+
 // GQ: the query map is not the identity (qmul, qadd) != (1, 0); a full layer
 // runs the GQ = false instance (compile-time identity map).
 // ROPE: q is rotated at its expanded position right after the load.
+//
+// Persistent: a launch has at most one workgroup per CU, and each walks a
+// list of items (query block of one group).  The items of an XCD are those
+// the non-persistent order would dispatch to it; a CU takes every
+// (32 CUs)-th of them in a snake order (c, 63-c, 64+c, ...), so that the
+// longest-first sequence gives each CU about the same number of tiles.
+// Between two items the next item's first K/V copies and its Q loads are
+// issued before the current item's output rows are stored, so the memory
+// latency that starts an item overlaps the end of the previous one and no
+// workgroup launch separates them.
+//
 // This function does the work-item map, loads Q, builds the per-lane LDS
 // address tables and copy offsets the key loop (sfa_fwd_d128_loop.inc) uses,
 // binds them to the registers the loop expects, and stores the output rows
@@ -278,62 +297,62 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
                                                                   float scale_log2) {
     constexpr int D = 128;
     constexpr int TILE = KT * D * 2;  // 16 KB per K or V tile
-    __shared__ __attribute__((aligned(1024))) char lds[6 * TILE];  // K ring (3 tiles) | V ring (3 tiles)
+    constexpr int OPITCH = 272;       // bytes per staged output row (16-byte aligned, spreads the banks)
+    // K ring (3 tiles) | V ring (3 tiles).  The output rows a wave leaves at
+    // the end of an item are staged from byte 4*TILE on (V ring buffers 1-2
+    // and beyond), clear of the buffers the next item's first copies fill
+    // (K 0, K 1, V 0); the next item's loop copies into V buffer 1 only
+    // after its first barrier, which every wave reaches once its own staged
+    // rows are read.
+    constexpr int STG = 4 * TILE;
+    __shared__ __attribute__((aligned(1024))) char lds[STG + D128_NW * D128_QW * OPITCH];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hi = lane >> 5, l16 = lane & 15, g2 = (lane >> 4) & 1;
     const int g = p.Hq / p.Hkv, ngrp = g / HG;
+    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
+    const int nwg = nrest * nqblk;
+    const int hw = wave % HG, tb = wave / HG;
+    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
+    const int64_t qrs = (int64_t)p.Hq * D;
+    const int64_t krs = (int64_t)p.Hkv * D;
+    const int QB = D128_QW * TB;
 
-    // Workgroup -> (query block, group).  Dispatch is round-robin over the 8
-    // XCDs (XCD bid % 8 runs its workgroups in bid order); the map keeps each
-    // XCD's share balanced (longest blocks first) and its groups few:
-    // whole groups per XCD when the group count is a multiple of 8 (the
+    // Item r of this workgroup, as the index of the non-persistent launch
+    // (nwg when there is none).  The launch has either one workgroup per
+    // item or a multiple of 8 workgroups, one per CU.
+    const int G = (int)gridDim.x;
+    auto item_bid = [&](int r) -> int {
+        if (G >= nwg) return r == 0 ? (int)blockIdx.x : nwg;
+        const int x = (int)blockIdx.x % 8, c = (int)blockIdx.x / 8, ncx = G / 8;
+        const int j = r * ncx + ((r & 1) ? ncx - 1 - c : c);
+        return min(x + 8 * j, nwg);
+    };
+    // Workgroup index -> (query block, group).  Dispatch is round-robin over
+    // the 8 XCDs (XCD bid % 8 runs its workgroups in bid order); the map
+    // keeps each XCD's share balanced (longest blocks first) and its groups
+    // few: whole groups per XCD when the group count is a multiple of 8 (the
     // XCD's groups taken two at a time, their blocks interleaved longest
     // first: one group at a time leaves a tail of short blocks, all of them
     // at once a K/V working set larger than the XCD's L2), each group spread
     // over 8/G XCDs when G divides 8, else round-robin.
-    const int nrest = p.B * p.Hkv * ngrp * p.nsub;
-    const int nwg = nrest * nqblk;
-    const int bid = blockIdx.x;
-    int lid = bid;
-    if (nwg % 8 == 0) {
-        const int x = bid % 8, j = bid / 8;
-        if (nrest % 8 == 0) {
-            const int gpx = nrest / 8;
-            const int iw = gpx % 2 == 0 ? 2 : gpx;  // groups interleaved at a time
-            const int ph = j / (iw * nqblk), jj = j % (iw * nqblk);
-            lid = (x * gpx + ph * iw + jj % iw) * nqblk + jj / iw;
-        } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
-            const int r = 8 / nrest;
-            lid = (x / r) * nqblk + j * r + x % r;
+    auto item_lid = [&](int bid) -> int {
+        int lid = bid;
+        if (nwg % 8 == 0) {
+            const int x = bid % 8, j = bid / 8;
+            if (nrest % 8 == 0) {
+                const int gpx = nrest / 8;
+                const int iw = gpx % 2 == 0 ? 2 : gpx;  // groups interleaved at a time
+                const int ph = j / (iw * nqblk), jj = j % (iw * nqblk);
+                lid = (x * gpx + ph * iw + jj % iw) * nqblk + jj / iw;
+            } else if (8 % nrest == 0 && nqblk % (8 / nrest) == 0) {
+                const int r = 8 / nrest;
+                lid = (x / r) * nqblk + j * r + x % r;
+            }
         }
-    }
-    const int qblk = nqblk - 1 - lid % nqblk;
-    int rest = lid / nqblk;
-    const int sub = rest % p.nsub; rest /= p.nsub;
-    const int hgrp = rest % ngrp; rest /= ngrp;
-    const int kvh = rest % p.Hkv;
-    const int b = rest / p.Hkv;
-
-    const int QB = D128_QW * TB;
-    const int q0 = qblk * QB;
-    const int hw = wave % HG, tb = wave / HG;
-    const int h = kvh * g + hgrp * HG + hw;
-    const int qw0 = q0 + tb * D128_QW;      // first query of this wave; half hf holds qw0 + 32 hf + l32
-    const int qmul = GQ ? p.qmul : 1, qadd = GQ ? p.qadd : 0;
-    const int lim0 = qw0 * qmul + qadd;                    // last key the wave's first query may see
-    const int lim1 = (qw0 + D128_QW - 1) * qmul + qadd;    // ... and its last
-
-    const int64_t qrs = (int64_t)p.Hq * D;
-    const int64_t krs = (int64_t)p.Hkv * D;
-    const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;              // key element 0
-    const int64_t qbase = (int64_t)b * p.qrows + (int64_t)sub * p.qsub;  // query 0's Q row
-
-    const int kend = min((min(q0 + QB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
-    const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
-    const int tfirst = kbeg & ~(KT - 1);
-    const int ntiles = (kend - tfirst + KT - 1) / KT;
+        return lid;
+    };
 
     // LDS address tables.  K operand of k-step ks (keys 0-31 of ring buffer
     // 0): row l32, 16-byte chunk (2ks + hi) ^ sw(row).  V^T half-operand
@@ -363,132 +382,249 @@ __global__ __launch_bounds__(64 * D128_NW, 1) void sfa_fwd_bf16_d128_kernel(FwdA
     // rows past the end of the sub-sequence re-reads its last row there
     // (finite data, masked in the loop).
     const int rstride = p.stride * (int)krs;  // elements between sub-sequence rows
-    unsigned boff[4], boffv[4], toff[4], toffv[4];
-    const int tlast = tfirst + (ntiles - 1) * KT;
-    const int rmax = p.Lsub - 1 - tlast;
+    const unsigned tbytes = (unsigned)(KT * rstride) * 2u;
+    const unsigned ldsw = ldsk + (unsigned)wave * 4096u;  // this wave's copy slots in a ring buffer
+    unsigned boff[4], boffv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int lrow = (wave * 4 + i) * 4 + (lane >> 4);
         const int lc = ((lane & 15) ^ swz128(lrow)) * 8, lcv = ((lane & 15) ^ swzv(lrow)) * 8;
         boff[i] = (unsigned)(lrow * rstride + lc) * 2u;
         boffv[i] = (unsigned)(lrow * rstride + lcv) * 2u;
-        toff[i] = (unsigned)(min(lrow, rmax) * rstride + lc) * 2u;
-        toffv[i] = (unsigned)(min(lrow, rmax) * rstride + lcv) * 2u;
     }
-    const int tailt = rmax < KT - 1 ? ntiles - 1 : -1;
-    const int64_t tile0 = (bpos + (int64_t)tfirst * p.stride) * krs + (int64_t)kvh * D;  // elements
-    const void *kptr = static_cast<const bf16 *>(p.k) + tile0;
-    const void *vptr = static_cast<const bf16 *>(p.v) + tile0;
-    const unsigned tbytes = (unsigned)(KT * rstride) * 2u;
-    const unsigned ldsw = ldsk + (unsigned)wave * 4096u;  // this wave's copy slots in a ring buffer
 
-    // Copies of K(0), K(1) and V(0), in flight while Q is loaded; the loop
-    // copies K(T+2) and V(T+1) at the start of tile T.
-    if (ntiles > 0) {
-        const char *k0 = static_cast<const char *>(kptr), *v0 = static_cast<const char *>(vptr);
+    // The 64 output rows of this wave are staged in LDS so that each store
+    // writes 16-byte pieces of whole 256-byte rows.
+    char *ost = lds + STG + wave * D128_QW * OPITCH;
+    const unsigned stg = lds_addr(ost) + l32 * OPITCH + 8 * hi;
+
+    // One item's work map: query block, head, first key tile and tile count,
+    // the tile whose rows run past the sub-sequence's end, K/V of tile 0.
+    struct Item {
+        int qw0, h, ntiles, tfirst, tailt, rmax, b, sub;
+        int64_t qbase;
+        const char *kptr, *vptr;
+    };
+    auto decode = [&](int lid) -> Item {
+        Item it;
+        const int qblk = nqblk - 1 - lid % nqblk;
+        int rest = lid / nqblk;
+        const int sub = rest % p.nsub; rest /= p.nsub;
+        const int hgrp = rest % ngrp; rest /= ngrp;
+        const int kvh = rest % p.Hkv;
+        const int b = rest / p.Hkv;
+        const int q0 = qblk * QB;
+        it.b = b;
+        it.sub = sub;
+        it.h = kvh * g + hgrp * HG + hw;
+        it.qw0 = q0 + tb * D128_QW;  // first query of this wave; half hf holds qw0 + 32 hf + l32
+        it.qbase = (int64_t)b * p.qrows + (int64_t)sub * p.qsub;  // query 0's Q row
+        const int64_t bpos = (int64_t)b * p.nL + p.kbase + sub;  // key element 0
+        const int kend = min((min(q0 + QB, p.Lq) - 1) * qmul + qadd + 1, p.Lsub);
+        const int kbeg = p.weff ? max(0, q0 * qmul + qadd - p.weff + 1) : 0;
+        it.tfirst = kbeg & ~(KT - 1);
+        it.ntiles = (kend - it.tfirst + KT - 1) / KT;
+        const int tlast = it.tfirst + (it.ntiles - 1) * KT;
+        it.rmax = p.Lsub - 1 - tlast;
+        it.tailt = it.rmax < KT - 1 ? it.ntiles - 1 : -1;
+        const int64_t tile0 = (bpos + (int64_t)it.tfirst * p.stride) * krs + (int64_t)kvh * D;  // elements
+        it.kptr = reinterpret_cast<const char *>(static_cast<const bf16 *>(p.k) + tile0);
+        it.vptr = reinterpret_cast<const char *>(static_cast<const bf16 *>(p.v) + tile0);
+        return it;
+    };
+    // Per-lane copy offsets of a tile whose rows run past the end.
+    auto tail_offsets = [&](const Item &it, unsigned *toff, unsigned *toffv) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16_s(k0, tailt == 0 ? toff[i] : boff[i], ldsw + i * 1024);
-        if (ntiles > 1) {
+        for (int i = 0; i < 4; ++i) {
+            const int lrow = (wave * 4 + i) * 4 + (lane >> 4);
+            const int lc = ((lane & 15) ^ swz128(lrow)) * 8, lcv = ((lane & 15) ^ swzv(lrow)) * 8;
+            toff[i] = (unsigned)(min(lrow, it.rmax) * rstride + lc) * 2u;
+            toffv[i] = (unsigned)(min(lrow, it.rmax) * rstride + lcv) * 2u;
+        }
+    };
+    // Copies of K(0), K(1) and V(0) of an item; its loop copies K(T+2) and
+    // V(T+1) at the start of tile T.
+    // (The item's fields are wave-uniform; readfirstlane says so to the
+    // compiler, which must pass them in scalar registers.)
+    auto first_copies = [&](const Item &it) {
+        if (it.ntiles <= 0) return;
+        unsigned toff[4], toffv[4];
+        tail_offsets(it, toff, toffv);
+        const char *kp = uniform_ptr(it.kptr), *vp = uniform_ptr(it.vptr);
+        const unsigned lw = (unsigned)__builtin_amdgcn_readfirstlane((int)ldsw);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_dma16_s(kp, it.tailt == 0 ? toff[i] : boff[i], lw + i * 1024);
+        if (it.ntiles > 1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                lds_dma16_s(k0 + tbytes, tailt == 1 ? toff[i] : boff[i], ldsw + TILE + i * 1024);
+                lds_dma16_s(kp + tbytes, it.tailt == 1 ? toff[i] : boff[i], lw + TILE + i * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) lds_dma16_s(v0, tailt == 0 ? toffv[i] : boffv[i], ldsw + 3 * TILE + i * 1024);
-    }
-    const void *kptr2 = static_cast<const char *>(kptr) + 2 * (size_t)tbytes;
-    const void *vptr1 = static_cast<const char *>(vptr) + tbytes;
-
-    // Q of both halves and each half's band: key
-    // k visible <=> k - lo <= span (unsigned).
-    bf16x8 qop[2][D / 16];
-    int maskbase[2], span[2], lo[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-        const int myq = qw0 + 32 * hf + l32;
-        const bool qvalid = myq < p.Lq;
-        const int mylim = myq * qmul + qadd;
-        const bf16 *qp = static_cast<const bf16 *>(p.q) + (qbase + (int64_t)(qvalid ? myq : 0) * p.qstride) * qrs +
-                         (int64_t)h * D;
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-            bf16x8 x = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
-            qop[hf][ks] = qvalid ? x : bf16x8{};
-        }
-        if (ROPE) rope_rotate_q<D>(qop[hf], p.kbase + sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
-        lo[hf] = p.weff ? mylim - p.weff + 1 : 0;
-        span[hf] = min(mylim, p.Lsub - 1) - lo[hf];
-        maskbase[hf] = 4 * hi - lo[hf];
-    }
-    // The wave's 32-key sub-tiles that need the mask: j < jw (window start)
-    // or j >= jm (the diagonal or the end of the sub-sequence).
-    const int mfull = min(lim0, p.Lsub - 1) - 31 - tfirst;
-    const int jm = mfull >= 0 ? mfull / 32 + 1 : 0;
-    const int wfull = lim1 - p.weff - tfirst;
-    const int jw = (p.weff && wfull >= 0) ? wfull / 32 + 1 : 0;
-
-    // The 64 output rows of this wave are staged in LDS (free once every wave
-    // has left the loop) so that each store writes 16-byte pieces of whole
-    // 256-byte rows.
-    constexpr int OPITCH = 272;  // bytes per staged row (16-byte aligned, spreads the banks)
-    char *ost = lds + wave * D128_QW * OPITCH;
-    const unsigned stg = lds_addr(ost) + l32 * OPITCH + 8 * hi;
-    float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
-    if (ntiles > 0) {
-        asm volatile(HD_FWD_D128_LOOP
-                     : "+{v160}"(m0), "+{v161}"(m1), "+{v162}"(l0), "+{v163}"(l1)
-                     : "{v[96:99]}"(qop[0][0]), "{v[100:103]}"(qop[0][1]), "{v[104:107]}"(qop[0][2]),
-                       "{v[108:111]}"(qop[0][3]), "{v[112:115]}"(qop[0][4]), "{v[116:119]}"(qop[0][5]),
-                       "{v[120:123]}"(qop[0][6]), "{v[124:127]}"(qop[0][7]), "{v[128:131]}"(qop[1][0]),
-                       "{v[132:135]}"(qop[1][1]), "{v[136:139]}"(qop[1][2]), "{v[140:143]}"(qop[1][3]),
-                       "{v[144:147]}"(qop[1][4]), "{v[148:151]}"(qop[1][5]), "{v[152:155]}"(qop[1][6]),
-                       "{v[156:159]}"(qop[1][7]),
-                       "{v164}"(kaddr[0]), "{v165}"(kaddr[1]), "{v166}"(kaddr[2]), "{v167}"(kaddr[3]),
-                       "{v168}"(kaddr[4]), "{v169}"(kaddr[5]), "{v170}"(kaddr[6]), "{v171}"(kaddr[7]),
-                       "{v172}"(vaddr[0]), "{v173}"(vaddr[1]), "{v174}"(vaddr[2]), "{v175}"(vaddr[3]),
-                       "{v176}"(vaddr[4]), "{v177}"(vaddr[5]), "{v178}"(vaddr[6]), "{v179}"(vaddr[7]),
-                       "{v180}"(boff[0]), "{v181}"(boff[1]), "{v182}"(boff[2]), "{v183}"(boff[3]),
-                       "{v184}"(boffv[0]), "{v185}"(boffv[1]), "{v186}"(boffv[2]), "{v187}"(boffv[3]),
-                       "{v188}"(toff[0]), "{v189}"(toff[1]), "{v190}"(toff[2]), "{v191}"(toff[3]),
-                       "{v192}"(toffv[0]), "{v193}"(toffv[1]), "{v194}"(toffv[2]), "{v195}"(toffv[3]),
-                       "{v196}"(maskbase[0]), "{v197}"(maskbase[1]), "{v198}"(span[0]), "{v199}"(span[1]),
-                       "{v249}"(stg), [nt] "s"(ntiles), [kt0] "s"(tfirst), [kptr2] "s"(kptr2),
-                       [vptr1] "s"(vptr1), [tbytes] "s"(tbytes), [tailt] "s"(tailt), [jw] "s"(jw), [jm] "s"(jm),
-                       [sc] "s"(scale_log2), [ldsw] "s"(ldsw)
-                     : HD_FWD_D128_CLOBBERS);
-    } else {
-        // no key tile (an empty key range): zero rows
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                *reinterpret_cast<uint2 *>(ost + (hf * 32 + l32) * OPITCH + 8 * hi + 16 * i) = uint2{0, 0};
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-    }
-#pragma unroll
-    for (int i = 0; i < D128_QW / 4; ++i) {
-        const int row = 4 * i + (lane >> 4), c = lane & 15;
-        const uint4 x = *reinterpret_cast<const uint4 *>(ost + row * OPITCH + c * 16);
-        const int q = qw0 + row;
-        if (q < p.Lq) {
-            const int64_t qrow = qbase + (int64_t)q * p.qstride;
-            *reinterpret_cast<uint4 *>(reinterpret_cast<char *>(p.o) + (qrow * qrs + (int64_t)h * D) * 2 + c * 16) = x;
-        }
-    }
-    if (p.lse != nullptr && hi == 0) {
+        for (int i = 0; i < 4; ++i)
+            lds_dma16_s(vp, it.tailt == 0 ? toffv[i] : boffv[i], lw + 3 * TILE + i * 1024);
+    };
+    // Q of both halves; a row past the end loads row 0 and is zeroed
+    // before use (so that all 16 loads can be in flight together).
+    auto load_q = [&](const Item &it, bf16x8 (&qop)[2][D / 16]) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int myq = qw0 + 32 * hf + l32;
-            if (myq < p.Lq) {
-                const int64_t qrow = qbase + (int64_t)myq * p.qstride;
-                p.lse[((int64_t)b * p.Hq + h) * p.qrows + (qrow - (int64_t)b * p.qrows)] =
-                    (hf ? m1 : m0) * kLn2 + __logf(hf ? l1 : l0);
+            const int myq = it.qw0 + 32 * hf + l32;
+            const bf16 *qp = static_cast<const bf16 *>(p.q) +
+                             (it.qbase + (int64_t)(myq < p.Lq ? myq : 0) * p.qstride) * qrs + (int64_t)it.h * D;
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) qop[hf][ks] = *reinterpret_cast<const bf16x8 *>(qp + ks * 16 + 8 * hi);
+        }
+    };
+
+    int r = 0;
+    const int bid0 = item_bid(0);
+    if (bid0 >= nwg) return;
+    Item cur = decode(item_lid(bid0));
+    bf16x8 qop[2][D / 16];
+    first_copies(cur);
+    load_q(cur, qop);
+    for (;;) {
+        // Each half's band: key k visible <=> k - lo <= span (unsigned).
+        int maskbase[2], span[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int myq = cur.qw0 + 32 * hf + l32;
+            const int mylim = myq * qmul + qadd;
+            if (myq >= p.Lq) {
+#pragma unroll
+                for (int ks = 0; ks < D / 16; ++ks) qop[hf][ks] = bf16x8{};
+            }
+            if (ROPE) rope_rotate_q<D>(qop[hf], p.kbase + cur.sub + (int64_t)mylim * p.stride, p.rope_ft, hi);
+            const int lo = p.weff ? mylim - p.weff + 1 : 0;
+            span[hf] = min(mylim, p.Lsub - 1) - lo;
+            maskbase[hf] = 4 * hi - lo;
+        }
+        // The wave's 32-key sub-tiles that need the mask: j < jw (window
+        // start) or j >= jm (the diagonal or the end of the sub-sequence).
+        const int lim0 = cur.qw0 * qmul + qadd;                    // last key the wave's first query may see
+        const int lim1 = (cur.qw0 + D128_QW - 1) * qmul + qadd;    // ... and its last
+        const int mfull = min(lim0, p.Lsub - 1) - 31 - cur.tfirst;
+        const int jm = mfull >= 0 ? mfull / 32 + 1 : 0;
+        const int wfull = lim1 - p.weff - cur.tfirst;
+        const int jw = (p.weff && wfull >= 0) ? wfull / 32 + 1 : 0;
+
+        float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
+        if (cur.ntiles > 0) {
+            unsigned toff[4], toffv[4];
+            tail_offsets(cur, toff, toffv);
+            const void *kptr2 = cur.kptr + 2 * (size_t)tbytes;
+            const void *vptr1 = cur.vptr + tbytes;
+            const int ntiles = cur.ntiles, tfirst = cur.tfirst, tailt = cur.tailt;
+            asm volatile(HD_FWD_D128_LOOP
+                         : "+{v160}"(m0), "+{v161}"(m1), "+{v162}"(l0), "+{v163}"(l1)
+                         : "{v[96:99]}"(qop[0][0]), "{v[100:103]}"(qop[0][1]), "{v[104:107]}"(qop[0][2]),
+                           "{v[108:111]}"(qop[0][3]), "{v[112:115]}"(qop[0][4]), "{v[116:119]}"(qop[0][5]),
+                           "{v[120:123]}"(qop[0][6]), "{v[124:127]}"(qop[0][7]), "{v[128:131]}"(qop[1][0]),
+                           "{v[132:135]}"(qop[1][1]), "{v[136:139]}"(qop[1][2]), "{v[140:143]}"(qop[1][3]),
+                           "{v[144:147]}"(qop[1][4]), "{v[148:151]}"(qop[1][5]), "{v[152:155]}"(qop[1][6]),
+                           "{v[156:159]}"(qop[1][7]),
+                           "{v164}"(kaddr[0]), "{v165}"(kaddr[1]), "{v166}"(kaddr[2]), "{v167}"(kaddr[3]),
+                           "{v168}"(kaddr[4]), "{v169}"(kaddr[5]), "{v170}"(kaddr[6]), "{v171}"(kaddr[7]),
+                           "{v172}"(vaddr[0]), "{v173}"(vaddr[1]), "{v174}"(vaddr[2]), "{v175}"(vaddr[3]),
+                           "{v176}"(vaddr[4]), "{v177}"(vaddr[5]), "{v178}"(vaddr[6]), "{v179}"(vaddr[7]),
+                           "{v180}"(boff[0]), "{v181}"(boff[1]), "{v182}"(boff[2]), "{v183}"(boff[3]),
+                           "{v184}"(boffv[0]), "{v185}"(boffv[1]), "{v186}"(boffv[2]), "{v187}"(boffv[3]),
+                           "{v188}"(toff[0]), "{v189}"(toff[1]), "{v190}"(toff[2]), "{v191}"(toff[3]),
+                           "{v192}"(toffv[0]), "{v193}"(toffv[1]), "{v194}"(toffv[2]), "{v195}"(toffv[3]),
+                           "{v196}"(maskbase[0]), "{v197}"(maskbase[1]), "{v198}"(span[0]), "{v199}"(span[1]),
+                           "{v249}"(stg), [nt] "s"(ntiles), [kt0] "s"(tfirst), [kptr2] "s"(kptr2),
+                           [vptr1] "s"(vptr1), [tbytes] "s"(tbytes), [tailt] "s"(tailt), [jw] "s"(jw),
+                           [jm] "s"(jm), [sc] "s"(scale_log2), [ldsw] "s"(ldsw)
+                         : HD_FWD_D128_CLOBBERS);
+        } else {
+            // no key tile (an empty key range): zero rows
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    *reinterpret_cast<uint2 *>(ost + (hf * 32 + l32) * OPITCH + 8 * hi + 16 * i) = uint2{0, 0};
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        }
+
+        // The next item's first copies and Q loads go out before this item's
+        // rows are stored (the loop above has passed its last barrier, so the
+        // ring buffers they fill are free).
+        const int bidn = item_bid(++r);
+        const bool more = bidn < nwg;
+        Item nxt = cur;
+        if (more) {
+            nxt = decode(item_lid(bidn));
+            first_copies(nxt);
+            load_q(nxt, qop);
+        }
+
+        // All staged rows are read first, then stored (without a per-row
+        // branch when every row of the wave is in range), so the reads and
+        // the stores each go out back to back.
+        {
+            // (one asm block with its own wait: the compiler, short of
+            // registers here, would otherwise wait for each read in turn)
+            static_assert(D128_QW / 4 == 16 && 15 * 4 * OPITCH < 65536, "staged-row reads below");
+            u32x4 x[D128_QW / 4];
+            const unsigned ra = lds_addr(ost) + (lane >> 4) * OPITCH + (lane & 15) * 16;
+            asm volatile(
+                "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1088\n\t"
+                "ds_read_b128 %2, %16 offset:2176\n\tds_read_b128 %3, %16 offset:3264\n\t"
+                "ds_read_b128 %4, %16 offset:4352\n\tds_read_b128 %5, %16 offset:5440\n\t"
+                "ds_read_b128 %6, %16 offset:6528\n\tds_read_b128 %7, %16 offset:7616\n\t"
+                "ds_read_b128 %8, %16 offset:8704\n\tds_read_b128 %9, %16 offset:9792\n\t"
+                "ds_read_b128 %10, %16 offset:10880\n\tds_read_b128 %11, %16 offset:11968\n\t"
+                "ds_read_b128 %12, %16 offset:13056\n\tds_read_b128 %13, %16 offset:14144\n\t"
+                "ds_read_b128 %14, %16 offset:15232\n\tds_read_b128 %15, %16 offset:16320\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7]),
+                  "=v"(x[8]), "=v"(x[9]), "=v"(x[10]), "=v"(x[11]), "=v"(x[12]), "=v"(x[13]), "=v"(x[14]),
+                  "=v"(x[15])
+                : "v"(ra)
+                : "memory");
+            char *orow = reinterpret_cast<char *>(p.o) +
+                         ((cur.qbase + (int64_t)(cur.qw0 + (lane >> 4)) * p.qstride) * qrs + (int64_t)cur.h * D) * 2 +
+                         (lane & 15) * 16;
+            const int64_t step = 4 * (int64_t)p.qstride * qrs * 2;  // bytes between rows 4 apart
+            if (cur.qw0 + D128_QW <= p.Lq) {
+#pragma unroll
+                for (int i = 0; i < D128_QW / 4; ++i) *reinterpret_cast<u32x4 *>(orow + i * step) = x[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < D128_QW / 4; ++i)
+                    if (cur.qw0 + 4 * i + (lane >> 4) < p.Lq) *reinterpret_cast<u32x4 *>(orow + i * step) = x[i];
             }
         }
+        if (p.lse != nullptr && hi == 0) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int myq = cur.qw0 + 32 * hf + l32;
+                if (myq < p.Lq) {
+                    const int64_t qrow = cur.qbase + (int64_t)myq * p.qstride;
+                    p.lse[((int64_t)cur.b * p.Hq + cur.h) * p.qrows + (qrow - (int64_t)cur.b * p.qrows)] =
+                        (hf ? m1 : m0) * kLn2 + __logf(hf ? l1 : l0);
+                }
+            }
+        }
+        if (!more) break;
+        cur = nxt;
     }
 }
 
 }  // namespace
+
+// Compute units of the current device (read once per device).
+static int device_cu_count() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
     const int g = a.Hq / a.Hkv;
@@ -519,7 +655,11 @@ hipError_t launch_sfa_fwd_bf16(const FwdArgs &a, hipStream_t st) {
                 const bool gq = a.qmul != 1 || a.qadd != 0;
                 auto kern = gq ? (a.rope ? sfa_fwd_bf16_d128_kernel<true, true> : sfa_fwd_bf16_d128_kernel<true, false>)
                                : (a.rope ? sfa_fwd_bf16_d128_kernel<false, true> : sfa_fwd_bf16_d128_kernel<false, false>);
-                hipLaunchKernelGGL(kern, dim3((unsigned)grid2), dim3(64 * D128_NW), 0, st, a, HG, TB2, nqblk2, sl2);
+                // one workgroup per CU (a multiple of 8, one per XCD in turn) when
+                // there are more items than CUs
+                const int ncu = device_cu_count() & ~7;
+                const int64_t grid3 = (ncu >= 8 && grid2 > ncu) ? ncu : grid2;
+                hipLaunchKernelGGL(kern, dim3((unsigned)grid3), dim3(64 * D128_NW), 0, st, a, HG, TB2, nqblk2, sl2);
             }
             break;
         default:
