@@ -63,6 +63,44 @@ def build_probe(verbose=False):
     return PROBE_LIB
 
 
+_ROCTX = None
+
+
+def _roctx():
+    """The ROCm tools-extension library (range markers a profiler's
+    --marker-trace records), or False where it is not installed."""
+    global _ROCTX
+    if _ROCTX is None:
+        _ROCTX = False
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                lib = ctypes.CDLL(name)
+            except OSError:
+                continue
+            lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            lib.roctxRangePushA.restype = ctypes.c_int
+            lib.roctxRangePop.argtypes = []
+            lib.roctxRangePop.restype = ctypes.c_int
+            _ROCTX = lib
+            break
+    return _ROCTX
+
+
+def marker_push(text):
+    """Open a named range around a timed loop, so that a kernel trace taken
+    with markers attributes each dispatch to its bench row (host-side only;
+    two calls per timed loop)."""
+    lib = _roctx()
+    if lib:
+        lib.roctxRangePushA(text.encode())
+
+
+def marker_pop():
+    lib = _roctx()
+    if lib:
+        lib.roctxRangePop()
+
+
 def _tri(T, w):
     """Sum over q in [0, T) of min(q + 1, w) (w = 0: no window)."""
     if w <= 0 or w >= T:
@@ -542,11 +580,13 @@ def main():
         torch.cuda.synchronize()
         s_ev = torch.cuda.Event(enable_timing=True)
         e_ev = torch.cuda.Event(enable_timing=True)
+        marker_push("timed:" + ",".join(group))
         s_ev.record()
         for _ in range(steps):
             for name, (fn, _, _) in group.items():
                 tm.run(name, fn)
         e_ev.record()
+        marker_pop()
         tm.collect()
         return s_ev.elapsed_time(e_ev)
 
