@@ -260,8 +260,11 @@ __global__ __launch_bounds__(256) void sfa_fwd_bf16_kernel(FwdArgs p, int HG, in
 //     dot instruction would stall the matrix core);
 //   * the loop's last step scales O by 1/l and writes the bf16 rows to LDS,
 //     so that every global store writes 16-byte pieces of whole rows;
-//   * workgroups are ordered so each XCD (round-robin dispatch) walks whole
-//     (batch, kv head, stream) groups, keeping that group's K/V in its L2.
+//   * items (query block x group) are ordered so each XCD (round-robin
+//     dispatch) walks whole (batch, kv head, stream) groups, keeping that
+//     group's K/V in its L2; with more items than CUs the launch is
+//     persistent (one workgroup per CU walking its share of the XCD's items,
+//     see the kernel below).
 constexpr int D128_NW = 4;  // waves per workgroup of the head-dim-128 kernel (one per SIMD)
 constexpr int D128_QW = 64; // queries per wave (two 32-query halves)
 
