@@ -176,6 +176,10 @@ MANY_WG_SHAPES = [
     ((3, 1984, 1, 12, 3, 128), INTRA, 0),   # 279 workgroups: count not a multiple of 8
     ((4, 600, 4, 8, 8, 128), CROSS, 0),     # 320 workgroups, MHA (g = 1)
     ((1, 1024, 4, 16, 4, 128), CROSS, 0),   # 4 groups: each spread over two XCDs
+    # persistent launch with several items per CU: 768 items (3 rounds of
+    # 256, 24 groups: three per XCD), ragged last block, windowed
+    ((3, 2000, 4, 8, 2, 128), INTRA, 200),
+    ((2, 1500, 4, 8, 2, 128), CROSS, 100),  # 376 items, 4 groups, window edges inside tiles
 ]
 
 
