@@ -697,10 +697,13 @@ def main():
                    "heads_q": 32, "heads_kv": 8, "head_dim": 128},
         "n4_n1_time_ratio": ratio,
         # the layers' useful-FLOP ratio beside it: a time ratio below it means
-        # the n=1 control runs less efficiently (512 workgroups on 256 CUs),
-        # not that the n=4 layer beats linear cost
+        # the n=1 control runs less efficiently (512 items on 256 CUs: two
+        # per CU, balanced less finely than the n=4 layer's eight), not that
+        # the n=4 layer beats linear cost
         "n4_n1_flop_ratio": (round(comps["intra_n4"][1] / comps["intra_n1"][1], 3)
                              if "intra_n4" in comps and "intra_n1" in comps else None),
+        "n4_n1_note": ("time ratio below the useful-FLOP ratio: the n=1 control runs at a lower TFLOP/s "
+                       "(components intra_n1 vs intra_n4), not a sub-linear n=4 layer"),
         # forward + backward of the attention layer (the pages compare training
         # step times); 4.0 would be the FLOP ratio
         "n4_n1_train_time_ratio": (round((report["intra_n4"]["ms"] + report["bwd_intra_n4"]["ms"]) /
